@@ -1,0 +1,227 @@
+"""Seeded synthetic workloads for the absorbed MLA decode path.
+
+This module holds random draws and memory layout only -- none of the method's
+arithmetic.  Both sides of every parity check (the CPU oracle and the HIP
+library) are fed the arrays built here, so that neither side generates inputs
+for the other.
+
+Workload geometry follows the pages' statement of the problem:
+
+* "MLA in full detail" (mlinterviewnotes), shapes table: kv_lora_rank 512,
+  nope 128, rope 64, v_head 128, 128 heads (DeepSeek-V3).
+* mlxcel "MLA absorbed decode", bytes table: DeepSeek-V2-Lite has 16 heads.
+* "M5.8 - Multi-Head Latent Attention", 0x05 "Paged and ragged address
+  translation": a logical token j lives at physical row
+  block_table[b, j // P] * P + j % P of a paged cache of 576-wide rows.
+
+Recipe (fixed draw order, numpy ``Generator(PCG64(seed))``):
+
+1. seqlens (ragged workloads only): L_b = clip(round(exp(U(ln lo, ln hi))), lo, hi)
+2. q_nope [B,T,H,128]  ~ N(0, 1)
+3. q_pe   [B,T,H,64]   ~ N(0, 1)   (already rotated; RoPE itself is upstream)
+4. W_UK   [H,128,512]  ~ N(0, 1/512)   (variance 1/512, std 1/sqrt(512))
+5. W_UV   [H,128,512]  ~ N(0, 1/512)
+6. physical block permutation (identity when ``permute`` is False)
+7. cache rows [num_blocks, P, 576] ~ N(0, 1)
+
+Every float32 draw is encoded to bfloat16 with round-to-nearest-even; arrays
+of bf16 values are returned as their uint16 bit patterns.  With ``poison``
+set, every cache row that no sequence may read (unused physical blocks, and
+the rows of a sequence's last page at or past its length) is overwritten with
+a bf16 quiet NaN so that any stray read surfaces as NaN in the output.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+R_LATENT = 512   # kv_lora_rank
+D_ROPE = 64      # qk_rope_head_dim
+D_NOPE = 128     # qk_nope_head_dim
+D_V = 128        # v_head_dim
+ROW = R_LATENT + D_ROPE  # 576 values per cached row
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Input values must be finite (they are normal draws here)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Workload:
+    """Shape recipe of one decode workload."""
+    name: str
+    B: int
+    T: int
+    H: int
+    L: int                      # per-sequence length (max length when ragged)
+    page_size: int
+    seed: int
+    num_splits: int = 1
+    permute: bool = True        # physical pages a seeded permutation
+    ragged: Optional[tuple] = None   # (lo, hi) log-uniform lengths
+    unused_frac: float = 0.0    # fraction of physical blocks left unused
+    contiguous: bool = False    # one block holding the whole sequence
+    lengths: Optional[tuple] = None  # explicit per-sequence lengths (overrides L)
+    r: int = R_LATENT
+    d_rope: int = D_ROPE
+    d_nope: int = D_NOPE
+    d_v: int = D_V
+    w_std: Optional[float] = None    # weight std; default 1/sqrt(r)
+
+    def describe(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["workload"] = d.pop("name")
+        return d
+
+
+# The five decode workloads (sizes as stated by the workload table of the
+# pages' geometry; see module docstring for the distributions).
+WORKLOADS = {
+    "v2lite_tiny": Workload("v2lite_tiny", B=1, T=1, H=16, L=256, page_size=256,
+                            seed=1001, permute=False, contiguous=True),
+    "v3_b64_l4096": Workload("v3_b64_l4096", B=64, T=1, H=128, L=4096, page_size=64,
+                             seed=1002),
+    "v3_ragged_b128": Workload("v3_ragged_b128", B=128, T=1, H=128, L=16384, page_size=64,
+                               seed=1003, ragged=(64, 16384), unused_frac=0.10),
+    "v3_long_b4_l131072": Workload("v3_long_b4_l131072", B=4, T=1, H=128, L=131072,
+                                   page_size=64, seed=1004, num_splits=64),
+    "v3_mtp_b32_t4_h32": Workload("v3_mtp_b32_t4_h32", B=32, T=4, H=32, L=8192,
+                                  page_size=64, seed=1005),
+}
+
+
+@dataclasses.dataclass
+class Case:
+    """Materialised inputs of one workload (host numpy arrays)."""
+    wl: Workload
+    q_nope: np.ndarray      # [B,T,H,128] uint16 (bf16 bits)
+    q_pe: np.ndarray        # [B,T,H,64]  uint16
+    w_uk: np.ndarray        # [H,128,512] uint16
+    w_uv: np.ndarray        # [H,128,512] uint16
+    kv_cache: np.ndarray    # [num_blocks,P,576] uint16
+    block_table: np.ndarray  # [B,max_blocks] int32, -1 past each sequence's pages
+    seqlens: np.ndarray     # [B] int32 (includes the T current rows)
+    used_blocks: np.ndarray  # sorted physical ids that some sequence maps
+
+    @property
+    def B(self): return self.wl.B
+
+    @property
+    def T(self): return self.wl.T
+
+    @property
+    def H(self): return self.wl.H
+
+    @property
+    def page_size(self): return self.wl.page_size
+
+    @property
+    def num_blocks(self): return self.kv_cache.shape[0]
+
+    @property
+    def max_blocks(self): return self.block_table.shape[1]
+
+    @property
+    def max_seqlen(self): return int(self.seqlens.max())
+
+
+def _normal_bf16(rng, shape, std=1.0):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return f32_to_bf16_bits(x)
+
+
+def make_case(wl: Workload, poison: bool = True) -> Case:
+    """Draw every input of ``wl`` from its seed (see module docstring)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    B, T, H, P = wl.B, wl.T, wl.H, wl.page_size
+    if wl.lengths is not None:
+        seqlens = np.asarray(wl.lengths, dtype=np.int32)
+        if seqlens.shape != (B,):
+            raise ValueError("lengths must give one length per sequence")
+    elif wl.ragged is not None:
+        lo, hi = wl.ragged
+        u = rng.uniform(math.log(lo), math.log(hi), size=B)
+        seqlens = np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+    else:
+        seqlens = np.full(B, wl.L, dtype=np.int32)
+    if (seqlens < T).any():
+        raise ValueError("every sequence must hold at least its T current rows")
+    r, dr, dn, dv = wl.r, wl.d_rope, wl.d_nope, wl.d_v
+    q_nope = _normal_bf16(rng, (B, T, H, dn))
+    q_pe = _normal_bf16(rng, (B, T, H, dr))
+    std_w = wl.w_std if wl.w_std is not None else 1.0 / math.sqrt(r)
+    w_uk = _normal_bf16(rng, (H, dn, r), std_w)
+    w_uv = _normal_bf16(rng, (H, dv, r), std_w)
+
+    pages = [(int(L) + P - 1) // P for L in seqlens]
+    max_blocks = max((int(seqlens.max()) + P - 1) // P, 1)
+    n_used = sum(pages)
+    if wl.contiguous:
+        if B != 1 or pages[0] != 1:
+            raise ValueError("a contiguous workload is one sequence in one block")
+        n_phys = 1
+    elif wl.unused_frac > 0:
+        n_phys = int(math.ceil(n_used / (1.0 - wl.unused_frac)))
+    else:
+        n_phys = n_used
+    perm = rng.permutation(n_phys).astype(np.int32) if wl.permute else np.arange(n_phys, dtype=np.int32)
+    block_table = np.full((B, max_blocks), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        for p in range(pages[b]):
+            block_table[b, p] = perm[k]
+            k += 1
+    used = np.sort(perm[:n_used])
+
+    kv_cache = _normal_bf16(rng, (n_phys, P, r + dr))
+    if poison:
+        mask = np.ones(n_phys, dtype=bool)
+        mask[used] = False
+        kv_cache[mask] = BF16_NAN
+        for b in range(B):
+            tail = int(seqlens[b]) % P
+            if tail:
+                kv_cache[block_table[b, pages[b] - 1], tail:, :] = BF16_NAN
+    return Case(wl, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, used)
+
+
+def scaled(wl: Workload, **changes) -> Workload:
+    """A copy of ``wl`` with some fields changed (reduced parity variants)."""
+    return dataclasses.replace(wl, **changes)
+
+
+def identity_paged_copy(case: Case) -> Case:
+    """Same logical contents, physical pages laid out in (b, page) order.
+
+    Used to check that the result depends only on the logical tokens, never on
+    where the pages sit."""
+    P = case.page_size
+    B = case.B
+    pages = [(int(L) + P - 1) // P for L in case.seqlens]
+    n = sum(pages)
+    cache = np.empty((n,) + case.kv_cache.shape[1:], dtype=np.uint16)
+    table = np.full_like(case.block_table, -1)
+    k = 0
+    for b in range(B):
+        for p in range(pages[b]):
+            cache[k] = case.kv_cache[case.block_table[b, p]]
+            table[b, p] = k
+            k += 1
+    return dataclasses.replace(case, kv_cache=cache, block_table=table,
+                               used_blocks=np.arange(n, dtype=np.int32))

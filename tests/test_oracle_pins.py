@@ -1,0 +1,415 @@
+"""Pins of the CPU oracle to facts fixed outside itself (no GPU).
+
+What pins what:
+* the numpy parity script printed on "MLA in full detail" (expanded and
+  absorbed scores/outputs agree in float64; scale (key+rope)^-0.5; row-vector
+  weight orientation) -- rebuilt here from its printed shapes and seed;
+* an independent numpy Normal path and PyTorch's float64
+  scaled_dot_product_attention on explicitly expanded K/V (library special case);
+* associativity: absorbed mirror == Normal path (M5.8 0x04);
+* closed forms: one visible key, zero queries (uniform weights, lse = ln n),
+  identical rows;
+* invariants: split merge == unsplit (M5.8 0x0C), page permutation invariance
+  (M5.8 0x05), determinism across thread counts;
+* negative controls: the mistakes M5.8 0x04 and mlxcel Stage 2 name must fail
+  the product tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle import costs
+
+
+def tol(ref):
+    """Product tolerance: max|err| <= 1e-2 * max|ref| + 1e-3."""
+    return 1e-2 * float(np.nanmax(np.abs(ref))) + 1e-3
+
+
+def tiny(seed, B=2, T=1, H=3, lengths=None, L=37, P=8, r=16, dr=4, dn=8, dv=6,
+         permute=True, unused=0.0, w_std=None):
+    wl = synth.Workload("tiny", B=B, T=T, H=H, L=L, page_size=P, seed=seed,
+                        permute=permute, unused_frac=unused,
+                        lengths=lengths, r=r, d_rope=dr, d_nope=dn, d_v=dv, w_std=w_std)
+    return synth.make_case(wl)
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# 1. the page's own parity script
+
+def test_page_numpy_script_shapes_and_identity():
+    """"MLA in full detail", numpy parity script: queries 3, context 5, rank 4,
+    key_dim 2, value_dim 3, rope_dim 2, seed 42.  The script states its identity
+    with row vectors (k = c @ uk); the oracle stores W_UK[h] = uk^T
+    (column convention of M5.8 0x04).  Each query sees all 5 keys, which the
+    oracle expresses as 3 sequences of length 5 with T = 1."""
+    rng = np.random.default_rng(42)
+    queries, context, rank, key_dim, value_dim, rope_dim = 3, 5, 4, 2, 3, 2
+    c = rng.normal(size=(context, rank))
+    q = rng.normal(size=(queries, key_dim))
+    q_rope = rng.normal(size=(queries, rope_dim))
+    k_rope = rng.normal(size=(context, rope_dim))
+    uk = rng.normal(size=(rank, key_dim))
+    uv = rng.normal(size=(rank, value_dim))
+    bf = lambda x: synth.f32_to_bf16_bits(x.astype(np.float32))
+    f = lambda bits: oracle.bf16_to_f64(bits)
+    c_b, q_b, qr_b, kr_b, uk_b, uv_b = map(bf, (c, q, q_rope, k_rope, uk, uv))
+    # the script's formulas on the same (bf16-representable) values
+    C, Q, QR, KR, UK, UV = map(f, (c_b, q_b, qr_b, kr_b, uk_b, uv_b))
+    scale = (key_dim + rope_dim) ** -0.5
+    expanded_scores = (Q @ (C @ UK).T + QR @ KR.T) * scale
+    absorbed_scores = ((Q @ UK.T) @ C.T + QR @ KR.T) * scale
+    np.testing.assert_allclose(absorbed_scores, expanded_scores, atol=1e-12)
+    e = np.exp(expanded_scores - expanded_scores.max(-1, keepdims=True))
+    a = e / e.sum(-1, keepdims=True)
+    script_out = a @ (C @ UV)
+    np.testing.assert_allclose(script_out, (a @ C) @ UV, atol=1e-12)
+    script_lse = np.log(np.exp(expanded_scores).sum(-1))
+
+    # same numbers through the oracle
+    from types import SimpleNamespace
+    row = np.concatenate([c_b, kr_b], axis=1)           # [5, rank + rope]
+    case = SimpleNamespace(
+        B=queries, T=1, H=1, page_size=8, num_blocks=1, max_blocks=1,
+        q_nope=q_b.reshape(queries, 1, 1, key_dim), q_pe=qr_b.reshape(queries, 1, 1, rope_dim),
+        w_uk=np.ascontiguousarray(uk_b.T).reshape(1, key_dim, rank),
+        w_uv=np.ascontiguousarray(uv_b.T).reshape(1, value_dim, rank),
+        kv_cache=np.concatenate([row, np.zeros((3, rank + rope_dim), np.uint16)]).reshape(1, 8, -1),
+        block_table=np.zeros((queries, 1), np.int32), seqlens=np.full(queries, context, np.int32))
+    out, lse = oracle.normal_decode(case)
+    np.testing.assert_allclose(out[:, 0, 0, :], script_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, 0, 0], script_lse, rtol=0, atol=1e-12)
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, lse2 = oracle.latent_attention(case, ql)
+    np.testing.assert_allclose(lat[:, 0, 0, :], a @ C, atol=1e-12)
+    out2 = oracle.unabsorb(lat, case.w_uv)
+    np.testing.assert_allclose(out2[:, 0, 0, :], script_out, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse, atol=1e-12)
+
+
+def test_page_causal_pair_count_from_uniform_weights():
+    """With zero queries every visible key gets the same weight, so exp(lse)
+    counts the visible keys of each query row.  3 new tokens after a prefix of
+    5 give 3*5 + 3*4/2 = 21 pairs ("MLA in full detail", numpy script)."""
+    case = tiny(3, B=1, T=3, H=2, lengths=(8,))
+    case.q_nope[:] = 0
+    case.q_pe[:] = 0
+    _, lse = oracle.normal_decode(case)
+    counts = np.exp(lse)
+    assert np.allclose(counts[0, :, 0], [6, 7, 8], atol=1e-12)
+    assert round(float(counts[..., 0].sum())) == 21 == costs.causal_pairs(3, 5)
+
+
+def test_causal_pairs_mtp_geometry_formula():
+    """Pairs of T new tokens over lengths L_b: sum_b H * (T*(L_b-T) + T*(T+1)/2);
+    checked on a reduced multi-token case against the oracle's uniform weights."""
+    case = tiny(4, B=3, T=4, H=2, lengths=(9, 23, 4), P=4)
+    case.q_nope[:] = 0
+    case.q_pe[:] = 0
+    _, lse = oracle.normal_decode(case)
+    total = float(np.exp(lse).sum())
+    want = sum(2 * costs.causal_pairs(4, int(L) - 4) for L in case.seqlens)
+    assert abs(total - want) < 1e-9
+    # the 32 x 4 x 32 x 8192 multi-token workload: 33,548,288 visible pairs
+    assert 32 * 32 * costs.causal_pairs(4, 8192 - 4) == 33_548_288
+
+
+# --------------------------------------------------------------------------
+# 2. independent implementations of the same definition
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_normal_matches_numpy_expanded(seed):
+    case = tiny(seed, B=3, T=2, H=4, lengths=(37, 9, 20), P=8, unused=0.2)
+    out, lse = oracle.normal_decode(case)
+    ref, ref_lse = oracle.expanded_attention_f64(case)
+    assert rel(out, ref) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+def test_normal_matches_torch_sdpa_float64():
+    """Library special case: the Normal path is exactly MHA over expanded K/V
+    (M5.8 0x05 naive path), so torch's float64 SDPA must reproduce it."""
+    case = tiny(21, B=2, T=3, H=4, lengths=(30, 13), P=8)
+    out, _ = oracle.normal_decode(case)
+    qn = oracle.bf16_to_f64(case.q_nope)
+    qp = oracle.bf16_to_f64(case.q_pe)
+    wk = oracle.bf16_to_f64(case.w_uk)
+    wv = oracle.bf16_to_f64(case.w_uv)
+    dn, dr, dv, r = oracle.dims(case)
+    for b, rows in enumerate(oracle.gather_rows(case)):
+        L = rows.shape[0]
+        c, kpe = rows[:, :r], rows[:, r:]
+        K = np.concatenate([np.einsum("hnc,jc->hjn", wk, c),
+                            np.broadcast_to(kpe[None], (case.H, L, dr))], axis=-1)
+        V = np.einsum("hvc,jc->hjv", wv, c)
+        Q = np.concatenate([qn[b], qp[b]], axis=-1).transpose(1, 0, 2)   # [H,T,192']
+        mask = np.zeros((case.T, L), dtype=bool)
+        for t in range(case.T):
+            mask[t, : L - case.T + t + 1] = True
+        got = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q), torch.from_numpy(np.ascontiguousarray(K)),
+            torch.from_numpy(V), attn_mask=torch.from_numpy(mask),
+            scale=1.0 / math.sqrt(dn + dr)).numpy()
+        assert rel(out[b].transpose(1, 0, 2), got) < 1e-12
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_absorbed_mirror_equals_normal(T):
+    """Associativity (M5.8 0x04; mlxcel: "without changing the arithmetic")."""
+    case = tiny(31 + T, B=3, T=T, H=5, lengths=(40, 17, 5), P=8)
+    out, lse = oracle.normal_decode(case)
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, lse2 = oracle.latent_attention(case, ql)
+    out2 = oracle.unabsorb(lat, case.w_uv)
+    assert rel(out2, out) < 1e-12
+    assert np.max(np.abs(lse2 - lse)) < 1e-12
+
+
+def test_absorbed_mirror_equals_normal_real_dims():
+    case = synth.make_case(synth.scaled(synth.WORKLOADS["v3_b64_l4096"], B=2, L=100, H=4, seed=5))
+    out, lse = oracle.normal_decode(case)
+    lat, lse2 = oracle.latent_attention(case, oracle.absorb(case.q_nope, case.w_uk))
+    assert rel(oracle.unabsorb(lat, case.w_uv), out) < 1e-12
+    assert np.max(np.abs(lse2 - lse)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# 3. closed-form special cases
+
+def test_single_visible_key_returns_its_value():
+    case = tiny(41, B=2, T=1, H=3, lengths=(1, 1), P=8)
+    out, lse = oracle.normal_decode(case)
+    dn, dr, dv, r = oracle.dims(case)
+    wk = oracle.bf16_to_f64(case.w_uk)
+    wv = oracle.bf16_to_f64(case.w_uv)
+    for b, rows in enumerate(oracle.gather_rows(case)):
+        c, kpe = rows[0, :r], rows[0, r:]
+        for h in range(case.H):
+            np.testing.assert_allclose(out[b, 0, h], wv[h] @ c, rtol=0, atol=1e-13)
+            s = (oracle.bf16_to_f64(case.q_nope[b, 0, h]) @ (wk[h] @ c)
+                 + oracle.bf16_to_f64(case.q_pe[b, 0, h]) @ kpe) / math.sqrt(dn + dr)
+            assert abs(lse[b, 0, h] - s) < 1e-12
+
+
+def test_zero_query_gives_mean_of_visible_latents():
+    case = tiny(42, B=2, T=2, H=2, lengths=(19, 6), P=4)
+    case.q_nope[:] = 0
+    case.q_pe[:] = 0
+    lat, lse = oracle.latent_attention(case, np.zeros(case.q_nope.shape[:3] + (case.w_uk.shape[2],)))
+    dn, dr, dv, r = oracle.dims(case)
+    for b, rows in enumerate(oracle.gather_rows(case)):
+        L = rows.shape[0]
+        for t in range(case.T):
+            vis = L - case.T + t + 1
+            np.testing.assert_allclose(lat[b, t, 0], rows[:vis, :r].mean(0), atol=1e-13)
+            assert abs(lse[b, t, 1] - math.log(vis)) < 1e-13
+
+
+def test_identical_rows_return_that_row_for_any_query():
+    """Weights sum to one: with every visible latent equal to c, out_latent == c."""
+    case = tiny(43, B=1, T=2, H=3, lengths=(21,), P=8)
+    row = case.kv_cache[case.block_table[0, 0], 0].copy()
+    for p in range(3):
+        case.kv_cache[case.block_table[0, p], :] = row
+    dn, dr, dv, r = oracle.dims(case)
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, _ = oracle.latent_attention(case, ql)
+    c = oracle.bf16_to_f64(row[:r])
+    np.testing.assert_allclose(lat[0], np.broadcast_to(c, lat[0].shape), atol=1e-13, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# 4. invariants
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64])
+def test_split_merge_equals_unsplit(S):
+    """M5.8 0x0C exact merge; chunks cut at page multiples, empty ones allowed."""
+    case = tiny(51, B=3, T=2, H=3, lengths=(57, 9, 33), P=8)
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, lse = oracle.latent_attention(case, ql)
+    plan = oracle.split_plan(case.seqlens, S, case.page_size)
+    ind, beg, end = plan
+    assert ind[-1] == 3 * S
+    if S == 64:
+        assert (beg == end).any()            # empty trailing splits exist
+    po, pl = oracle.latent_attention(case, ql, plan=plan)
+    m, ml = oracle.merge(po, pl, ind)
+    assert not np.isnan(m).any()
+    assert rel(m, lat) < 1e-12
+    assert np.max(np.abs(ml - lse)) < 1e-12
+
+
+def test_split_plan_rule():
+    ind, beg, end = oracle.split_plan(np.array([131072, 100, 64], np.int32), 64, 64)
+    assert list(ind) == [0, 64, 128, 192]
+    assert beg[1] == 2048 and end[63] == 131072           # 64 chunks of 2048 tokens
+    assert beg[64] == 0 and end[64] == 64 and beg[65] == 64 and end[65] == 100
+    assert (beg[66:128] == 100).all() and (end[66:128] == 100).all()
+
+
+def test_page_permutation_is_invisible_bitwise():
+    case = tiny(61, B=3, T=2, H=2, lengths=(40, 17, 25), P=8, unused=0.3)
+    ident = synth.identity_paged_copy(case)
+    assert not np.array_equal(case.block_table, ident.block_table)
+    a, la = oracle.normal_decode(case)
+    b, lb = oracle.normal_decode(ident)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_thread_count_does_not_change_bits():
+    case = tiny(62, B=2, T=2, H=4, lengths=(30, 19), P=8)
+    a, la = oracle.normal_decode(case, nthreads=1)
+    b, lb = oracle.normal_decode(case, nthreads=5)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_pairs_subset_matches_full_run():
+    case = tiny(63, B=3, T=1, H=4, lengths=(22, 9, 30), P=8)
+    full, lf = oracle.normal_decode(case)
+    pairs = np.array([[2, 3], [0, 1]], np.int32)
+    part, lp = oracle.normal_decode(case, pairs=pairs)
+    for b, h in pairs:
+        assert np.array_equal(part[b, :, h], full[b, :, h])
+    assert np.isnan(part[1]).all()
+
+
+def test_paged_address_formula():
+    """M5.8 0x05: physical(j) = block_table[b, j // P] * P + j % P; a negative
+    page entry (or one past the pool) is rejected."""
+    bt = np.array([[3, 1, -1], [0, 2, 4]], np.int32)
+    assert oracle.phys_row(bt, 0, 0, 4, 5) == 12
+    assert oracle.phys_row(bt, 0, 5, 4, 5) == 5
+    assert oracle.phys_row(bt, 0, 8, 4, 5) == -1
+    assert oracle.phys_row(bt, 1, 11, 4, 5) == 4 * 4 + 3
+    assert oracle.phys_row(bt, 1, 11, 4, 4) == -1   # pool of 4 blocks: id 4 is out of range
+
+
+def test_bad_block_table_is_an_error():
+    case = tiny(64, B=2, T=1, H=2, lengths=(20, 12), P=8)
+    case.block_table[1, 1] = -1
+    with pytest.raises(RuntimeError):
+        oracle.normal_decode(case)
+
+
+# --------------------------------------------------------------------------
+# 5. the input recipe
+
+def test_score_variance_is_one_under_the_recipe():
+    """Reading N(0, 1/512) as variance 1/512 makes the scaled scores unit
+    variance: 128 * (1/512) * 512 + 64 = 192, divided by 192."""
+    case = synth.make_case(synth.scaled(synth.WORKLOADS["v3_b64_l4096"], B=2, L=512, seed=77))
+    ql = oracle.absorb(case.q_nope, case.w_uk)          # [2,1,128,512]
+    rows = oracle.gather_rows(case)
+    s = []
+    for b in range(2):
+        c, kpe = rows[b][:, :512], rows[b][:, 512:]
+        qp = oracle.bf16_to_f64(case.q_pe[b, 0])
+        s.append((ql[b, 0] @ c.T + qp @ kpe.T) / math.sqrt(192))
+    var = float(np.var(np.concatenate([x.ravel() for x in s])))
+    assert abs(var - 1.0) < 0.05
+
+
+# --------------------------------------------------------------------------
+# 6. negative controls: each planted mistake must fail the product tolerance
+
+def _real_small():
+    return synth.make_case(synth.scaled(synth.WORKLOADS["v3_b64_l4096"], B=2, T=2, L=24, H=8,
+                                        page_size=16, seed=91))
+
+
+def _mirror(case, scale=None, softmax_axis="keys", share_heads=False, flip_wuv=False,
+            extra_key=False):
+    """numpy absorbed decode with one selectable mistake (CPU only)."""
+    dn, dr, dv, r = oracle.dims(case)
+    scale = 1.0 / math.sqrt(dn + dr) if scale is None else scale
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    qp = oracle.bf16_to_f64(case.q_pe)
+    wv = oracle.bf16_to_f64(case.w_uv)
+    if flip_wuv:
+        wv = wv[:, :, ::-1]
+    out = np.zeros((case.B, case.T, case.H, dv))
+    cache = oracle.bf16_to_f64(case.kv_cache).reshape(-1, r + dr)
+    for b in range(case.B):
+        L = int(case.seqlens[b])
+        n = L + 1 if extra_key else L
+        idx = [int(case.block_table[b, j // case.page_size]) * case.page_size + j % case.page_size
+               for j in range(n)]
+        rows = cache[idx]
+        c, kpe = rows[:, :r], rows[:, r:]
+        s = (np.einsum("thc,jc->thj", ql[b], c) + np.einsum("thr,jr->thj", qp[b], kpe)) * scale
+        for t in range(case.T):
+            s[t, :, n - case.T + t + 1:] = -np.inf
+        if softmax_axis == "keys":
+            p = np.exp(s - s.max(-1, keepdims=True))
+            p /= p.sum(-1, keepdims=True)
+        else:   # over heads
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            p = np.nan_to_num(p)
+        lat = np.einsum("thj,jc->thc", p, c)
+        if share_heads:
+            lat[:] = lat.mean(1, keepdims=True)
+        out[b] = np.einsum("thc,hvc->thv", lat, wv)
+    return out
+
+
+@pytest.fixture(scope="module")
+def small_ref():
+    case = _real_small()
+    out, _ = oracle.normal_decode(case)
+    return case, out
+
+
+def _fails(got, ref):
+    err = np.max(np.abs(got - ref)) if not np.isnan(got).any() else np.inf
+    return err > tol(ref)
+
+
+def test_mirror_without_mistake_passes(small_ref):
+    case, ref = small_ref
+    assert not _fails(_mirror(case), ref)
+
+
+@pytest.mark.parametrize("mistake", [
+    dict(softmax_axis="heads"),          # M5.8 0x04 bug 1
+    dict(share_heads=True),              # M5.8 0x04 bug 2
+    dict(flip_wuv=True),                 # M5.8 0x04 bug 3 (d_c axis differs between factors)
+    dict(scale=1.0 / math.sqrt(576)),    # "MLA in full detail": latent-width scale changes the function
+    dict(extra_key=True),                # reading past the visible length (poisoned row)
+])
+def test_negative_control_fails(small_ref, mistake):
+    case, ref = small_ref
+    assert _fails(_mirror(case, **mistake), ref)
+
+
+def test_averaging_partials_fails():
+    """M5.8 0x0C: averaging split outputs is wrong."""
+    case = _real_small()
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, _ = oracle.latent_attention(case, ql)
+    plan = oracle.split_plan(case.seqlens, 2, case.page_size)
+    po, pl = oracle.latent_attention(case, ql, plan=plan)
+    avg = po.reshape(case.B, 2, *po.shape[1:]).mean(1)
+    assert _fails(avg, lat)
+
+
+def test_log2_lse_units_fail():
+    """mlxcel Stage 2: mixing log2 and natural-log LSE units merges into a
+    plausible but wrong average; the merge must see natural logs."""
+    case = _real_small()
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, _ = oracle.latent_attention(case, ql)
+    plan = oracle.split_plan(case.seqlens, 2, case.page_size)
+    po, pl = oracle.latent_attention(case, ql, plan=plan)
+    good, _ = oracle.merge(po, pl, plan[0])
+    assert not _fails(good, lat)
+    wrong, _ = oracle.merge(po, pl * math.log2(math.e), plan[0])
+    assert _fails(wrong, lat)
