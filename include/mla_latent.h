@@ -1,0 +1,171 @@
+/*
+ * mla_latent.h -- C ABI of the matrix-absorbed MLA decode path on MI355X (gfx950).
+ *
+ * The four compute entry points follow the order of the absorbed decode:
+ *
+ *   mla_absorb_q       q~ = W_UK^T q_nope              ("MLA in full detail", Step 2:
+ *                                                       fold W_UK into the query)
+ *   mla_decode_latent  attention of all query heads against one shared paged
+ *                      latent cache of [c (512) || k_pe (64)] rows; score
+ *                      (q~ . c + q_pe . k_pe) * scale, softmax over the key
+ *                      axis, output the softmax-weighted sum of the 512-wide
+ *                      latents, optionally as split-KV partial states
+ *                                                      (same page, Step 3: attend
+ *                                                       against the latent directly;
+ *                                                       M5.8 0x05 paged address
+ *                                                       translation; M5.8 0x08 lse output)
+ *   mla_merge_splits   exact log-sum-exp merge of the split partials
+ *                                                      (M5.8 0x0C sequence-split merge;
+ *                                                       mlxcel Stage 2 merge contract)
+ *   mla_unabsorb_out   out = W_UV latent                ("MLA in full detail", Step 4:
+ *                                                       fold W_UV into the output)
+ *
+ * "M5.8" is the page "M5.8 - Multi-Head Latent Attention: Latent KV State,
+ * Weight Absorption, and FlashMLA"; "mlxcel" is its "MLA absorbed decode" page.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers to caller-owned, row-major, contiguous
+ *    memory.  bf16 tensors are passed as uint16_t storage of bfloat16 values.
+ *    Every pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    validate host-side scalars and pointers, enqueue their kernels on `stream`
+ *    and return; they never synchronise, never allocate device memory and keep
+ *    no state between calls.  Calls on different streams that share no output
+ *    buffer may run concurrently.
+ *  - The return value is MLA_OK or a negative mla_status.  On a negative return
+ *    nothing has been enqueued, except MLA_ERR_LAUNCH, which reports a failed
+ *    kernel launch (hipGetLastError) after validation passed.
+ *  - Device-resident index data (block tables, sequence lengths) is trusted by
+ *    the compute entry points: an out-of-range entry is undefined behaviour.
+ *    mla_validate_inputs checks it (synchronously) for callers that need that.
+ *
+ * Fixed geometry of this build: kv_lora_rank r = 512, rope width d_R = 64,
+ * d_nope = d_V = 128.  H (query heads) is 1..128, T (query tokens per
+ * sequence) is 1..8, page_size is a multiple of 16 in [16, 1024].
+ */
+#ifndef MLA_LATENT_H
+#define MLA_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,          /* a required pointer is NULL */
+  MLA_ERR_ALIGN = -2,         /* a pointer is not 16-byte aligned */
+  MLA_ERR_SHAPE = -3,         /* a size is out of range or sizes disagree */
+  MLA_ERR_UNSUPPORTED = -4,   /* geometry outside what this build implements */
+  MLA_ERR_WORKSPACE = -5,     /* workspace or partial buffers too small / missing */
+  MLA_ERR_LAUNCH = -6,        /* a kernel launch failed */
+  MLA_ERR_INVALID_INDEX = -7, /* (mla_validate_inputs) bad block-table entry or length */
+  MLA_ERR_DEVICE = -8         /* HIP runtime error while querying the device */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+/* Absorb: q_lat[b,t,h,c] = sum_{n<d_nope} q_nope[b,t,h,n] * W_UK[h,n,c], accumulated
+ * in fp32 and rounded to bf16 (nearest-even).
+ *   q_nope  [B,T,H,d_nope] bf16        w_uk [H,d_nope,r] bf16
+ *   q_lat   [B,T,H,r]      bf16 (out)
+ * Source: "MLA in full detail", Step 2 (the bmm [N,B,P] x [N,P,L] -> [N,B,L]);
+ * M5.8 0x04 "Batched absorption trace" (einsum bhqn,hnc->bhqc; W_UK [H,d_N,d_c]). */
+int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, int B, int T,
+                 int H, int d_nope, int r, void* stream);
+
+/* Sizes the caller must provide for mla_decode_latent with `num_splits`:
+ *   *workspace_bytes  -- bytes of the `workspace` argument (0 when num_splits == 1);
+ *   *max_total_splits -- rows of part_out / part_lse (0 when num_splits == 1).
+ * num_splits: 1 = no split; S > 1 = every sequence cut into S chunks (see
+ * mla_decode_latent); 0 = automatic (split counts chosen on the device from the
+ * sequence lengths so that the work fills the GPU's compute units).
+ * Queries the current HIP device (compute-unit count) when num_splits == 0. */
+int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int page_size,
+                              int num_splits, size_t* workspace_bytes, int* max_total_splits);
+
+/* Absorbed latent attention over a paged cache.
+ *   q_lat       [B,T,H,r]    bf16   absorbed query (mla_absorb_q)
+ *   q_pe        [B,T,H,d_R]  bf16   rope part of the query, already rotated
+ *   kv_cache    [num_blocks,page_size,r+d_R] bf16; row = [c (r) || k_pe (d_R)], one
+ *               latent KV head shared by all query heads (1152-byte rows)
+ *   block_table [B,max_blocks_per_seq] int32: physical block of each logical page;
+ *               logical token j of sequence b is row block_table[b, j/page_size] *
+ *               page_size + j%page_size (M5.8 0x05).  Entries at or past
+ *               ceil(seqlens[b]/page_size) are never read.
+ *   seqlens     [B] int32: visible rows per sequence, INCLUDING the T current
+ *               rows; T <= seqlens[b] <= max_seqlen.  Query t of sequence b sees
+ *               keys j <= seqlens[b] - T + t (causal over the current rows;
+ *               M5.8 0x05: a query at position p sees p + 1 rows).
+ *   softmax_scale  the caller passes 1/sqrt(d_nope + d_R) = 1/sqrt(192)
+ *               ("MLA in full detail", numpy parity script: the scale of the
+ *               original 192-wide key is kept).
+ *   num_splits  1: single pass, writes out_latent and lse.
+ *               S > 1: sequence b is cut into S contiguous chunks of
+ *               ceil(ceil(seqlens[b]/S)/page_size)*page_size tokens (trailing
+ *               chunks may be empty); chunk s writes its partial state to row
+ *               split_indptr[b] + s of part_out / part_lse.
+ *               0: automatic split counts (see mla_decode_workspace_size).
+ *   workspace   device scratch of the size reported by mla_decode_workspace_size;
+ *               may be NULL when num_splits == 1.  Contents on entry are ignored.
+ *   part_out    [max_total_splits,T,H,r] f32: partial outputs, each divided by its
+ *               own softmax denominator (mlxcel Stage 2 contract)
+ *   part_lse    [max_total_splits,T,H] f32: natural-log LSE of each partial;
+ *               -inf for an empty chunk (whose part_out row is zero)
+ *   split_indptr [B+1] int32 (out): first partial row of each sequence
+ *   out_latent  [B,T,H,r] bf16 or f32 (out_dtype).  With num_splits == 1 it
+ *               receives the result.  With num_splits != 1 it may be NULL (the
+ *               caller runs mla_merge_splits later); when non-NULL the
+ *               partials are merged on the device before the call returns
+ *               (stream order) and out_latent / lse receive the merged result.
+ *   lse         [B,T,H] f32 natural-log LSE of each query row; nullable.
+ * Returns MLA_ERR_WORKSPACE when num_splits != 1 and workspace, part_out,
+ * part_lse or split_indptr is missing or workspace_bytes is too small. */
+int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                      int num_blocks, int page_size, const int32_t* block_table,
+                      int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
+                      int d_R, int max_seqlen, float softmax_scale, int num_splits,
+                      void* workspace, size_t workspace_bytes, float* part_out, float* part_lse,
+                      int32_t* split_indptr, void* out_latent, mla_dtype out_dtype, float* lse,
+                      void* stream);
+
+/* Merge of split partial states, per (b,t,h) over rows k in
+ * [split_indptr[b], split_indptr[b+1]):  M = max_k lse_k, w_k = exp(lse_k - M),
+ * lse = M + log(sum_k w_k), out = sum_k w_k * part_out[k] / sum_k w_k.  Rows with
+ * lse_k = -inf carry no weight.  Natural-log units only: an LSE in log2 units
+ * merges into a plausible but wrong average (mlxcel Stage 2).
+ *   part_out [*,T,H,r] f32, part_lse [*,T,H] f32, split_indptr [B+1] int32
+ *   out_latent [B,T,H,r] bf16 or f32 (out_dtype), lse [B,T,H] f32 (nullable)
+ * Source: M5.8 0x0C (exact merge of (m_r, l_r, o_r); averaging is wrong). */
+int mla_merge_splits(const float* part_out, const float* part_lse, const int32_t* split_indptr,
+                     int B, int T, int H, int r, void* out_latent, mla_dtype out_dtype, float* lse,
+                     void* stream);
+
+/* Un-absorb: out[b,t,h,v] = sum_{c<r} latent[b,t,h,c] * W_UV[h,v,c]; latent is
+ * rounded to bf16 for the matrix cores when given as f32; fp32 accumulation.
+ *   latent [B,T,H,r] bf16 or f32 (latent_dtype)   w_uv [H,d_V,r] bf16
+ *   out    [B,T,H,d_V] f32
+ * Source: "MLA in full detail", Step 4 (bmm (N,B,L) x (N,L,V)); M5.8 0x04
+ * (einsum bhqc,hvc->bhqv; W_UV [H,d_V,d_c]). */
+int mla_unabsorb_out(const void* latent, mla_dtype latent_dtype, const uint16_t* w_uv, float* out,
+                     int B, int T, int H, int r, int d_V, void* stream);
+
+/* Synchronous check of the device-resident index data of mla_decode_latent:
+ * every needed block-table entry is in [0, num_blocks) and every seqlen is in
+ * [T, max_seqlen] with ceil(seqlen/page_size) <= max_blocks_per_seq.  Copies
+ * seqlens and the needed table entries to the host (blocking on `stream`).
+ * Returns MLA_OK or MLA_ERR_INVALID_INDEX.  For debugging and tests. */
+int mla_validate_inputs(const int32_t* block_table, int max_blocks_per_seq,
+                        const int32_t* seqlens, int B, int T, int max_seqlen, int page_size,
+                        int num_blocks, void* stream);
+
+/* Static string for a status code. */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LATENT_H */

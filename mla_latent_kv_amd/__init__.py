@@ -1,0 +1,236 @@
+"""Python binding of libmla_latent.so, the MI355X (gfx950) absorbed MLA decode path.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+behind the C ABI declared in ``include/mla_latent.h``.  PyTorch provides device
+memory (output tensors allocated here with ``torch.empty``) and the current HIP
+stream.  There is no fallback: if the shared library is missing or fails to
+load, importing the functions below raises.
+
+Entry points (same names as the C ABI):
+
+* ``mla_absorb_q``      q~ = W_UK^T q_nope                   ("MLA in full detail", Step 2)
+* ``mla_decode_latent`` latent attention over the paged cache ("MLA in full detail", Step 3)
+* ``mla_merge_splits``  log-sum-exp merge of split partials   (M5.8 0x0C)
+* ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
+* ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
+
+``absorbed_decode`` chains the four calls for one decode step.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_latent.so")
+
+MLA_BF16 = 0
+MLA_F32 = 1
+R_LATENT, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} (status {status})")
+
+
+def load_library():
+    """Load the in-tree shared library (built by ``mla_latent_kv_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run mla_latent_kv_amd._build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    SZ = ctypes.c_size_t
+    L.mla_status_string.argtypes = [I]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, I, P]
+    L.mla_decode_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ), ctypes.POINTER(I)]
+    L.mla_decode_latent.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I,
+                                    P, SZ, P, P, P, P, I, P, P]
+    L.mla_merge_splits.argtypes = [P, P, P, I, I, I, I, P, I, P, P]
+    L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
+    for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
+                 "mla_merge_splits", "mla_unabsorb_out", "mla_validate_inputs"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().mla_status_string(int(status)).decode()
+
+
+mla_status_string = status_string
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st, what):
+    if st != 0:
+        raise MLAError(st, what)
+
+
+def _dtype_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return MLA_BF16
+    if dtype == torch.float32:
+        return MLA_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def mla_absorb_q(q_nope, w_uk, q_lat=None, stream=None):
+    """q_nope [B,T,H,128] bf16, w_uk [H,128,512] bf16 -> q_lat [B,T,H,512] bf16."""
+    torch = _torch()
+    B, T, H, dn = q_nope.shape
+    r = w_uk.shape[2]
+    if q_lat is None:
+        q_lat = torch.empty((B, T, H, r), dtype=torch.bfloat16, device=q_nope.device)
+    _check(load_library().mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(q_lat), B, T, H, dn, r,
+                                       _stream(stream)), "mla_absorb_q")
+    return q_lat
+
+
+def mla_decode_workspace_size(B, T, H, max_seqlen, page_size, num_splits, r=R_LATENT):
+    """(workspace bytes, max_total_splits) for mla_decode_latent."""
+    nb = ctypes.c_size_t(0)
+    ms = ctypes.c_int(0)
+    _check(load_library().mla_decode_workspace_size(B, T, H, r, max_seqlen, page_size, num_splits,
+                                                    ctypes.byref(nb), ctypes.byref(ms)),
+           "mla_decode_workspace_size")
+    return int(nb.value), int(ms.value)
+
+
+class DecodeBuffers:
+    """Caller-owned scratch of mla_decode_latent in split mode (allocated once, reused)."""
+
+    def __init__(self, B, T, H, max_seqlen, page_size, num_splits, device):
+        torch = _torch()
+        nbytes, max_splits = mla_decode_workspace_size(B, T, H, max_seqlen, page_size, num_splits)
+        self.num_splits = num_splits
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        self.workspace_bytes = nbytes
+        self.part_out = torch.empty((max(max_splits, 1), T, H, R_LATENT), dtype=torch.float32,
+                                    device=device)
+        self.part_lse = torch.empty((max(max_splits, 1), T, H), dtype=torch.float32, device=device)
+        self.split_indptr = torch.empty(B + 1, dtype=torch.int32, device=device)
+
+
+def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                      num_splits=1, out_dtype=None, buffers: Optional[DecodeBuffers] = None,
+                      out_latent=None, lse=None, merge=True, stream=None):
+    """Absorbed latent attention (see include/mla_latent.h for the contract).
+
+    Returns (out_latent, lse).  With num_splits != 1 and merge=False the merge
+    is skipped, out_latent is None and the partials stay in ``buffers``."""
+    torch = _torch()
+    B, T, H, r = q_lat.shape
+    dr = q_pe.shape[3]
+    num_blocks, page_size, _ = kv_cache.shape
+    max_blocks = block_table.shape[1]
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    want_out = num_splits == 1 or merge
+    if want_out and out_latent is None:
+        out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
+    if want_out and lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q_lat.device)
+    if num_splits != 1 and buffers is None:
+        buffers = DecodeBuffers(B, T, H, max_seqlen, page_size, num_splits, q_lat.device)
+    ws = buffers.workspace if num_splits != 1 else None
+    st = load_library().mla_decode_latent(
+        _ptr(q_lat), _ptr(q_pe), _ptr(kv_cache), num_blocks, page_size, _ptr(block_table),
+        max_blocks, _ptr(seqlens), B, T, H, r, dr, int(max_seqlen), float(softmax_scale),
+        int(num_splits), _ptr(ws), buffers.workspace_bytes if num_splits != 1 else 0,
+        _ptr(buffers.part_out if num_splits != 1 else None),
+        _ptr(buffers.part_lse if num_splits != 1 else None),
+        _ptr(buffers.split_indptr if num_splits != 1 else None),
+        _ptr(out_latent if want_out else None), _dtype_code(out_dtype),
+        _ptr(lse if want_out else None), _stream(stream))
+    _check(st, "mla_decode_latent")
+    return (out_latent, lse) if want_out else (None, None)
+
+
+def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=None,
+                     out_dtype=None, stream=None):
+    """Merge partials -> (out_latent [B,T,H,512], lse [B,T,H])."""
+    torch = _torch()
+    _, T, H, r = part_out.shape
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_latent is None:
+        out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=part_out.device)
+    _check(load_library().mla_merge_splits(_ptr(part_out), _ptr(part_lse), _ptr(split_indptr), B, T,
+                                           H, r, _ptr(out_latent), _dtype_code(out_latent.dtype),
+                                           _ptr(lse), _stream(stream)), "mla_merge_splits")
+    return out_latent, lse
+
+
+def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
+    """latent [B,T,H,512] bf16/f32, w_uv [H,128,512] bf16 -> out [B,T,H,128] f32."""
+    torch = _torch()
+    B, T, H, r = latent.shape
+    dv = w_uv.shape[1]
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=latent.device)
+    _check(load_library().mla_unabsorb_out(_ptr(latent), _dtype_code(latent.dtype), _ptr(w_uv),
+                                           _ptr(out), B, T, H, r, dv, _stream(stream)),
+           "mla_unabsorb_out")
+    return out
+
+
+def mla_validate_inputs(block_table, seqlens, T, max_seqlen, page_size, num_blocks, stream=None):
+    """Synchronous index check; returns the status code (0 = valid)."""
+    B = seqlens.shape[0]
+    return int(load_library().mla_validate_inputs(_ptr(block_table), block_table.shape[1],
+                                                  _ptr(seqlens), B, T, int(max_seqlen), page_size,
+                                                  num_blocks, _stream(stream)))
+
+
+def softmax_scale(d_nope=D_NOPE, d_rope=D_ROPE) -> float:
+    """1/sqrt(d_nope + d_rope): the original 192-wide key's scale ("MLA in full detail")."""
+    return 1.0 / math.sqrt(d_nope + d_rope)
+
+
+def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, max_seqlen,
+                    num_splits=1, buffers=None, latent_dtype=None, stream=None):
+    """One decode step: absorb -> latent attention (-> merge) -> un-absorb.
+
+    Returns (out [B,T,H,128] f32, lse [B,T,H] f32)."""
+    torch = _torch()
+    q_lat = mla_absorb_q(q_nope, w_uk, stream=stream)
+    lat, lse = mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen,
+                                 softmax_scale(), num_splits=num_splits,
+                                 out_dtype=latent_dtype or torch.bfloat16, buffers=buffers,
+                                 stream=stream)
+    out = mla_unabsorb_out(lat, w_uv, stream=stream)
+    return out, lse
+
+
+__all__ = [
+    "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
+    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_merge_splits",
+    "mla_unabsorb_out", "mla_validate_inputs", "DecodeBuffers", "softmax_scale", "absorbed_decode",
+]

@@ -1,0 +1,84 @@
+// Device helpers shared by the gfx950 kernels of the absorbed MLA decode path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Geometry fixed by this build ("MLA in full detail", shapes table: kv_lora_rank 512,
+// rope 64, nope 128, v_head 128).
+constexpr int kR = 512;                 // latent width
+constexpr int kDR = 64;                 // rope width
+constexpr int kRow = kR + kDR;          // 576 values per cached row
+constexpr int kRowBytes = kRow * 2;     // 1152 bytes
+constexpr int kRowChunks = kRowBytes / 16;  // 72 chunks of 16 bytes
+constexpr int kDN = 128;
+constexpr int kDV = 128;
+constexpr int kTile = 16;               // tokens per KV tile
+constexpr int kTileBytes = kTile * kRowBytes;  // 18432
+constexpr int kRowsPerWG = 128;         // query rows (t, h) handled by one workgroup
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// float -> bf16 bits, round to nearest even (inputs here are finite or +-inf/NaN-free).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __builtin_bit_cast(float, ((uint32_t)h) << 16);
+}
+// two floats -> packed bf16x2 (low = a), nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// Operands are assembled from whole vectors (bit casts and shuffles), never by
+// inserting bf16 elements one at a time: the element-wise form has been seen to
+// compile to code that drops half of the values.
+__device__ __forceinline__ bf16x8 join8(s16x4 lo, s16x4 hi) {
+  return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1,
+                                 2, 3, 4, 5, 6, 7);
+}
+// eight floats -> eight bf16 (nearest even), element i of the result = input i
+__device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
+  u32x4 u;
+  u[0] = pack_bf16x2(lo[0], lo[1]);
+  u[1] = pack_bf16x2(lo[2], lo[3]);
+  u[2] = pack_bf16x2(hi[0], hi[1]);
+  u[3] = pack_bf16x2(hi[2], hi[3]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// 16-byte global -> LDS copy for every lane of the wave: lane i of the wave
+// writes LDS bytes [lds_addr + 16 i, lds_addr + 16 i + 16).  Issued as inline
+// assembly so that the compiler's wait-count pass does not serialise later
+// LDS reads behind it; the caller orders it with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Workgroup barrier without the memory fence that __syncthreads() adds (the
+// fence would also wait for the in-flight tile prefetches).
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+}  // namespace mla

@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint16_t* q_lat;       // [B,T,H,512] bf16
+  const uint16_t* q_pe;        // [B,T,H,64] bf16
+  const uint16_t* cache;       // [num_blocks,P,576] bf16
+  const int32_t* block_table;  // [B,max_blocks]
+  const int32_t* seqlens;      // [B]
+  const int32_t* work;         // split mode: [n][4] = (b, j0, j1, slot)
+  const int32_t* n_items;      // split mode: number of work items (device)
+  int B, T, H, page_size, max_blocks;
+  int n_rg;                    // workgroups per work item (ceil(T*H/128))
+  float scale_log2;            // softmax_scale * log2(e)
+  float* part_out;             // split mode: [*,T,H,512] f32
+  float* part_lse;             // split mode: [*,T,H] f32
+  void* out;                   // unsplit: [B,T,H,512] bf16 or f32
+  float* lse;                  // unsplit: [B,T,H] f32, nullable
+};
+
+struct PlanParams {
+  const int32_t* seqlens;
+  int B, num_splits, page_size;
+  int target_units, min_chunk, cap;  // automatic split policy
+  int32_t* work;
+  int32_t* n_items;
+  int32_t* split_indptr;
+};
+
+struct MergeParams {
+  const float* part_out;
+  const float* part_lse;
+  const int32_t* split_indptr;
+  int B, TH;
+  void* out;
+  float* lse;
+};
+
+struct AbsorbParams {
+  const uint16_t* q_nope;  // [M,H,128] (M = B*T)
+  const uint16_t* w_uk;    // [H,128,512]
+  uint16_t* q_lat;         // [M,H,512]
+  int M, H;
+};
+
+struct UnabsorbParams {
+  const void* latent;      // [M,H,512] bf16 or f32
+  const uint16_t* w_uv;    // [H,128,512]
+  float* out;              // [M,H,128]
+  int M, H;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int grid, bool split, bool out_f32, hipStream_t st);
+hipError_t launch_plan(const PlanParams& p, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, bool out_f32, hipStream_t st);
+hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);
+hipError_t launch_unabsorb(const UnabsorbParams& p, bool latent_f32, hipStream_t st);
+
+}  // namespace mla

@@ -225,3 +225,16 @@ def identity_paged_copy(case: Case) -> Case:
             k += 1
     return dataclasses.replace(case, kv_cache=cache, block_table=table,
                                used_blocks=np.arange(n, dtype=np.int32))
+
+
+def normal_bf16(shape, seed, std=1.0) -> np.ndarray:
+    """A standalone seeded N(0, std^2) bf16 array (stage inputs such as an
+    absorbed query or a latent output given directly to one stage)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _normal_bf16(rng, shape, std)
+
+
+def normal_f32(shape, seed, std=1.0) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return x * np.float32(std) if std != 1.0 else x

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/mla_latent.h declares, and rejects bad host-side arguments before any
+launch (the pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_amd as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_latent.h")
+
+OK, NULL, ALIGN, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mk.LIB_PATH):
+        from mla_latent_kv_amd import _build
+        _build.build()
+    return mk.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        s = mk.status_string(code)
+        assert s and s != "unknown status"
+    assert mk.status_string(12345) == "unknown status"
+
+
+P16 = ctypes.c_void_p(1 << 20)      # 16-byte aligned fake device address
+P17 = ctypes.c_void_p((1 << 20) + 2)  # misaligned
+
+
+def test_absorb_validation(lib):
+    f = lib.mla_absorb_q
+    assert f(P16, P16, P16, 2, 1, 128, 64, 512, None) == UNSUP     # d_nope != 128
+    assert f(P16, P16, P16, 2, 1, 128, 128, 256, None) == UNSUP    # r != 512
+    assert f(P16, P16, P16, 2, 9, 128, 128, 512, None) == UNSUP    # T > 8
+    assert f(P16, P16, P16, 2, 1, 129, 128, 512, None) == UNSUP    # H > 128
+    assert f(P16, P16, P16, 2, 0, 128, 128, 512, None) == SHAPE    # T < 1
+    assert f(P16, P16, P16, -1, 1, 128, 128, 512, None) == SHAPE
+    assert f(None, P16, P16, 2, 1, 128, 128, 512, None) == NULL
+    assert f(P16, P17, P16, 2, 1, 128, 128, 512, None) == ALIGN
+    assert f(None, None, None, 0, 1, 128, 128, 512, None) == OK    # empty batch: no-op
+
+
+def test_unabsorb_validation(lib):
+    f = lib.mla_unabsorb_out
+    assert f(P16, 0, P16, P16, 2, 1, 128, 512, 64, None) == UNSUP
+    assert f(P16, 7, P16, P16, 2, 1, 128, 512, 128, None) == UNSUP  # bad dtype
+    assert f(P16, 0, None, P16, 2, 1, 128, 512, 128, None) == NULL
+    assert f(P16, 1, P16, P17, 2, 1, 128, 512, 128, None) == ALIGN
+    assert f(None, 0, None, None, 0, 1, 128, 512, 128, None) == OK
+
+
+def _decode(lib, **kw):
+    a = dict(q_lat=P16, q_pe=P16, kv=P16, nb=64, P=64, bt=P16, mb=64, sl=P16, B=2, T=1, H=128,
+             r=512, dr=64, maxL=4096, scale=0.07, S=1, ws=None, wsb=0, po=None, pl=None, si=None,
+             out=P16, odt=0, lse=None)
+    a.update(kw)
+    return lib.mla_decode_latent(a["q_lat"], a["q_pe"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"],
+                                 a["sl"], a["B"], a["T"], a["H"], a["r"], a["dr"], a["maxL"],
+                                 ctypes.c_float(a["scale"]), a["S"], a["ws"], a["wsb"], a["po"],
+                                 a["pl"], a["si"], a["out"], a["odt"], a["lse"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, r=256) == UNSUP
+    assert _decode(lib, dr=32) == UNSUP
+    assert _decode(lib, P=24) == UNSUP          # not a multiple of 16
+    assert _decode(lib, P=2048) == UNSUP
+    assert _decode(lib, T=9) == UNSUP
+    assert _decode(lib, odt=5) == UNSUP
+    assert _decode(lib, scale=0.0) == SHAPE
+    assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, maxL=0, T=1) == SHAPE    # max_seqlen < T
+    assert _decode(lib, mb=63) == SHAPE          # 4096 tokens need 64 pages of 64
+    assert _decode(lib, nb=0) == SHAPE
+    assert _decode(lib, S=-1) == SHAPE
+    assert _decode(lib, q_lat=None) == NULL
+    assert _decode(lib, kv=P17) == ALIGN
+    assert _decode(lib, out=None) == NULL        # unsplit needs out_latent
+    assert _decode(lib, S=4) == WS               # split without workspace
+    need = ctypes.c_size_t(0)
+    ms = ctypes.c_int(0)
+    assert lib.mla_decode_workspace_size(2, 1, 128, 512, 4096, 64, 4, ctypes.byref(need),
+                                         ctypes.byref(ms)) == OK
+    assert ms.value == 8 and need.value >= 8 * 16
+    assert _decode(lib, S=4, ws=P16, wsb=need.value - 1, po=P16, pl=P16, si=P16) == WS
+    assert _decode(lib, S=4, ws=P16, wsb=need.value, po=P16, pl=P16, si=None) == WS
+    assert _decode(lib, B=0, q_lat=None, out=None) == OK
+
+
+def test_workspace_size(lib):
+    need = ctypes.c_size_t(123)
+    ms = ctypes.c_int(7)
+    assert lib.mla_decode_workspace_size(64, 1, 128, 512, 4096, 64, 1, ctypes.byref(need),
+                                         ctypes.byref(ms)) == OK
+    assert need.value == 0 and ms.value == 0
+    assert lib.mla_decode_workspace_size(4, 1, 128, 512, 131072, 64, 64, ctypes.byref(need),
+                                         ctypes.byref(ms)) == OK
+    assert ms.value == 256
+    assert lib.mla_decode_workspace_size(4, 1, 128, 512, 131072, 64, 64, None, ctypes.byref(ms)) == NULL
+    assert lib.mla_decode_workspace_size(4, 1, 128, 256, 131072, 64, 64, ctypes.byref(need),
+                                         ctypes.byref(ms)) == UNSUP
+
+
+def test_merge_validation(lib):
+    f = lib.mla_merge_splits
+    assert f(P16, P16, P16, 2, 1, 128, 256, P16, 0, None, None) == UNSUP
+    assert f(None, P16, P16, 2, 1, 128, 512, P16, 0, None, None) == NULL
+    assert f(P16, P16, P16, 2, 1, 128, 512, P17, 0, None, None) == ALIGN
+    assert f(P16, P16, P16, 2, 1, 128, 512, P16, 9, None, None) == UNSUP
+    assert f(None, None, None, 0, 1, 128, 512, None, 0, None, None) == OK
+
+
+def test_binding_names_match_abi():
+    for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out",
+              "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
+        assert callable(getattr(mk, n))

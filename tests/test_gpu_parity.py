@@ -1,0 +1,231 @@
+"""GPU parity of every entry point of the C ABI against the CPU oracle, on
+seeded inputs small enough for the oracle to run in full (several KV tiles,
+ragged tails, causal multi-token rows, more than 128 query rows, tiny and
+single-key sequences, page sizes 16/64/256).
+
+Stage inputs are generated, never taken from the GPU: the decode stage gets a
+seeded absorbed query, the un-absorb stage a seeded latent.  The end-to-end
+chain runs the GPU's own intermediates and is compared with the oracle's
+Normal (decompressed) path."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (SCALE, assert_close, bf16_tensor, bits_to_f64, log, to_f64, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mk():
+    import torch
+    import mla_latent_kv_amd as mk
+    mk.load_library()  # raises if the HIP library is missing
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return mk
+
+
+W = synth.WORKLOADS
+
+
+def small_cases():
+    return {
+        "v2lite_tiny": W["v2lite_tiny"],
+        "v3_b3_l300": synth.scaled(W["v3_b64_l4096"], B=3, L=300, seed=2101),
+        "v3_ragged_b5": synth.scaled(W["v3_ragged_b128"], B=5, ragged=None,
+                                     lengths=(1, 17, 64, 250, 1000), seed=2102),
+        "mtp_t4_h32": synth.scaled(W["v3_mtp_b32_t4_h32"], B=3, lengths=(100, 4, 77), seed=2103),
+        "t2_h128_rows256": synth.scaled(W["v3_b64_l4096"], B=2, T=2, lengths=(70, 33), seed=2104),
+        "h1_short": synth.scaled(W["v3_b64_l4096"], B=3, H=1, lengths=(1, 15, 16), seed=2105),
+        "page16_h64": synth.scaled(W["v3_b64_l4096"], B=2, H=64, page_size=16, lengths=(100, 47),
+                                   seed=2106),
+        "page256_h16": synth.scaled(W["v3_b64_l4096"], B=2, H=16, page_size=256,
+                                    lengths=(600, 257), seed=2107),
+    }
+
+
+CASES = small_cases()
+
+
+def _case(name):
+    return synth.make_case(CASES[name])
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_absorb(mk, name):
+    log(f"[absorb] {name}")
+    case = _case(name)
+    d = upload(case)
+    q_lat = mk.mla_absorb_q(d["q_nope"], d["w_uk"])
+    ref = oracle.absorb(case.q_nope, case.w_uk)
+    assert_close(to_f64(q_lat), ref, "q_lat")
+
+
+def _stage_q_lat(case, seed):
+    # absorbed queries are W_UK^T q_nope: N(0, 128/512) per element under the recipe
+    return synth.normal_bf16(case.q_nope.shape[:3] + (512,), seed, std=0.5)
+
+
+@pytest.mark.parametrize("out_f32", [True, False])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_unsplit(mk, name, out_f32):
+    import torch
+    log(f"[decode unsplit] {name} out_f32={out_f32}")
+    case = _case(name)
+    d = upload(case)
+    ql_bits = _stage_q_lat(case, 7000 + len(name))
+    q_lat = bf16_tensor(ql_bits, "cuda:0")
+    lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                    case.max_seqlen, SCALE, num_splits=1,
+                                    out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref_lat, ref_lse = oracle.latent_attention(case, bits_to_f64(ql_bits))
+    assert_close(to_f64(lat), ref_lat, "latent")
+    assert_close(to_f64(lse), ref_lse, "lse")
+
+
+@pytest.mark.parametrize("latent_f32", [True, False])
+@pytest.mark.parametrize("name", ["v3_b3_l300", "mtp_t4_h32", "h1_short", "v2lite_tiny"])
+def test_unabsorb(mk, name, latent_f32):
+    import torch
+    log(f"[unabsorb] {name} latent_f32={latent_f32}")
+    case = _case(name)
+    d = upload(case)
+    shape = case.q_nope.shape[:3] + (512,)
+    if latent_f32:
+        x = synth.normal_f32(shape, 8100, std=0.1)
+        lat = torch.from_numpy(x).to("cuda:0")
+        ref = oracle.unabsorb(x.astype(np.float64), case.w_uv)
+    else:
+        bits = synth.normal_bf16(shape, 8101, std=0.1)
+        lat = bf16_tensor(bits, "cuda:0")
+        ref = oracle.unabsorb(bits_to_f64(bits), case.w_uv)
+    out = mk.mla_unabsorb_out(lat, d["w_uv"])
+    assert_close(to_f64(out), ref, "out")
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_end_to_end_vs_normal_path(mk, name):
+    import torch
+    log(f"[end-to-end] {name}")
+    case = _case(name)
+    d = upload(case)
+    out, lse = mk.absorbed_decode(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"],
+                                  d["block_table"], d["seqlens"], case.max_seqlen)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.normal_decode(case)
+    assert_close(to_f64(out), ref, "out")
+    assert_close(to_f64(lse), ref_lse, "lse")
+
+
+@pytest.mark.parametrize("S", [2, 3, 7])
+@pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64"])
+def test_split_partials_and_merge(mk, name, S):
+    import torch
+    log(f"[split] {name} S={S}")
+    case = _case(name)
+    d = upload(case)
+    ql_bits = _stage_q_lat(case, 7100 + S)
+    q_lat = bf16_tensor(ql_bits, "cuda:0")
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, "cuda:0")
+    lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                    case.max_seqlen, SCALE, num_splits=S, out_dtype=torch.float32,
+                                    buffers=buf)
+    torch.cuda.synchronize()
+    plan = oracle.split_plan(case.seqlens, S, case.page_size)
+    # the split plan is integer work: bit-exact
+    assert np.array_equal(buf.split_indptr.cpu().numpy(), plan[0])
+    q64 = bits_to_f64(ql_bits)
+    ref_po, ref_pl = oracle.latent_attention(case, q64, plan=plan)
+    n = int(plan[0][-1])
+    got_pl = buf.part_lse[:n].cpu().numpy().astype(np.float64)
+    empty = np.isneginf(ref_pl)
+    assert np.array_equal(np.isneginf(got_pl), empty), "empty partials must carry lse = -inf"
+    assert_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
+    assert_close(buf.part_out[:n].cpu().numpy(), ref_po, "partial out")
+    ref_lat, ref_lse = oracle.latent_attention(case, q64)
+    assert_close(to_f64(lat), ref_lat, "merged latent")
+    assert_close(to_f64(lse), ref_lse, "merged lse")
+
+
+def test_auto_split(mk):
+    import torch
+    log("[split auto] v3_ragged_b5")
+    case = _case("v3_ragged_b5")
+    d = upload(case)
+    ql_bits = _stage_q_lat(case, 7200)
+    q_lat = bf16_tensor(ql_bits, "cuda:0")
+    lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                    case.max_seqlen, SCALE, num_splits=0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_lat, ref_lse = oracle.latent_attention(case, bits_to_f64(ql_bits))
+    assert_close(to_f64(lat), ref_lat, "latent")
+    assert_close(to_f64(lse), ref_lse, "lse")
+
+
+def test_merge_of_oracle_partials(mk):
+    """The merge kernel alone, fed partials the oracle computed (as f32)."""
+    import torch
+    log("[merge] oracle partials")
+    case = _case("mtp_t4_h32")
+    q64 = bits_to_f64(_stage_q_lat(case, 7300))
+    plan = oracle.split_plan(case.seqlens, 5, case.page_size)
+    po, pl = oracle.latent_attention(case, q64, plan=plan)
+    ref, ref_lse = oracle.merge(po, pl, plan[0])
+    dev = "cuda:0"
+    out, lse = mk.mla_merge_splits(torch.from_numpy(po.astype(np.float32)).to(dev),
+                                   torch.from_numpy(pl.astype(np.float32)).to(dev),
+                                   torch.from_numpy(plan[0]).to(dev), case.B,
+                                   out_dtype=torch.float32)
+    assert_close(to_f64(out), ref, "merged")
+    assert_close(to_f64(lse), ref_lse, "merged lse")
+
+
+def test_page_placement_is_bitwise_invisible(mk):
+    """Accumulation follows logical tokens, so moving pages changes no bit."""
+    import torch
+    log("[bitwise] permuted vs identity pages")
+    case = _case("v3_ragged_b5")
+    ident = synth.identity_paged_copy(case)
+    ql = bf16_tensor(_stage_q_lat(case, 7400), "cuda:0")
+    outs = []
+    for c in (case, ident):
+        d = upload(c)
+        lat, lse = mk.mla_decode_latent(ql, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                        c.max_seqlen, SCALE, out_dtype=torch.float32)
+        outs.append((lat.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_deterministic(mk):
+    import torch
+    log("[bitwise] repeat run")
+    case = _case("mtp_t4_h32")
+    d = upload(case)
+    res = []
+    for _ in range(2):
+        out, lse = mk.absorbed_decode(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"],
+                                      d["block_table"], d["seqlens"], case.max_seqlen, num_splits=3)
+        res.append((out.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+def test_validate_inputs(mk):
+    import torch
+    log("[validate]")
+    case = _case("v3_ragged_b5")
+    d = upload(case)
+    args = (1, case.max_seqlen, case.page_size, case.num_blocks)
+    assert mk.mla_validate_inputs(d["block_table"], d["seqlens"], *args) == 0
+    bad = case.block_table.copy()
+    bad[2, 0] = case.num_blocks          # out of the pool
+    assert mk.mla_validate_inputs(torch.from_numpy(bad).cuda(), d["seqlens"], *args) == -7
+    bad = case.block_table.copy()
+    bad[4, 3] = -1                       # a needed page left unmapped
+    assert mk.mla_validate_inputs(torch.from_numpy(bad).cuda(), d["seqlens"], *args) == -7
+    sl = case.seqlens.copy()
+    sl[1] = case.max_seqlen + 1
+    assert mk.mla_validate_inputs(d["block_table"], torch.from_numpy(sl).cuda(), *args) == -7
