@@ -1,0 +1,241 @@
+#!/usr/bin/env python
+"""Benchmark of the absorbed MLA decode step on one MI355X.
+
+One step = the whole path over one batch: absorb (q~ = W_UK^T q_nope) ->
+latent attention over the paged cache (split-KV partials) -> log-sum-exp merge
+-> un-absorb (W_UV latent).  Workload: DeepSeek-V3 geometry, B=64 sequences of
+L=4096 cached tokens, T=1, H=128, page size 64 with a seeded random page
+permutation, synthetic N(0,1) bf16 inputs and N(0,1/512) weights.
+
+Timing: W warm-up steps, then K steps between two device synchronisations.
+Three replicas of the cache and of the weights rotate from step to step so that
+the 256 MB last-level cache cannot serve a step's reads from the previous one.
+The decode kernel is also bracketed by HIP events on the launch stream to get
+its own duration, from which the roofline fraction is computed.
+
+Prints one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+ROW_BYTES = 1152                 # [c (512) || k_pe (64)] bf16
+HEADLINE = "v3_b64_l4096"
+
+
+def decode_algorithmic(case):
+    """Algorithmic bytes and FLOPs of one decode launch: every visible cache row
+    once (1152 B), the query (q~ 512 + q_pe 64, bf16), block table entries used,
+    lengths, the bf16 latent output and the fp32 lse; FLOPs 2*H*(576+512) per
+    visible (query, key) pair."""
+    import numpy as np
+    B, T, H, P = case.B, case.T, case.H, case.page_size
+    L = case.seqlens.astype(np.int64)
+    pairs = int(np.sum([T * (l - T) + T * (T + 1) // 2 for l in L]))   # visible (t, j) per sequence
+    rows = int(L.sum())
+    q_bytes = B * T * H * (512 + 64) * 2
+    table_bytes = int(np.sum((L + P - 1) // P)) * 4
+    out_bytes = B * T * H * 512 * 2 + B * T * H * 4
+    nbytes = rows * ROW_BYTES + q_bytes + table_bytes + B * 4 + out_bytes
+    flops = 2 * H * pairs * (576 + 512)
+    return nbytes, flops
+
+
+def chain_algorithmic(case, decode_bytes):
+    B, T, H = case.B, case.T, case.H
+    absorb = B * T * H * 128 * 2 + H * 128 * 512 * 2 + B * T * H * 512 * 2
+    unabsorb = B * T * H * 512 * 2 + H * 128 * 512 * 2 + B * T * H * 128 * 4
+    return decode_bytes + absorb + unabsorb
+
+
+def cpu_baseline(case, pairs_n, threads, seed=123):
+    """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
+    and scale linearly to the whole batch (its cost is linear in pairs x keys)."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    B, H = case.B, case.H
+    idx = rng.choice(B * H, size=min(pairs_n, B * H), replace=False)
+    pairs = np.stack([idx // H, idx % H], axis=1).astype(np.int32)
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.normal_decode(case, pairs=pairs, nthreads=threads)
+    dt = time.perf_counter() - t0
+    keys_sample = float(np.sum(case.seqlens[pairs[:, 0]]))
+    keys_all = float(np.sum(case.seqlens)) * H
+    t_full = dt * keys_all / keys_sample
+    return {
+        "value": case.B * case.T / t_full,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 Normal-path oracle on {len(pairs)} of {B * H} (sequence, head) pairs "
+                  f"({int(keys_sample)} keys, {dt:.1f} s on {threads} threads), scaled linearly "
+                  f"to all {B * H} pairs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--splits", type=int, default=4,
+                    help="split-KV chunks per sequence (0 = automatic)")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-pairs", type=int, default=640)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path does not shard across GPUs "
+              "(one process, one device); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_amd as mk
+    import synth
+
+    mk.load_library()
+    dev = "cuda:0"
+    wl = synth.WORKLOADS[args.workload]
+    case = synth.make_case(wl, poison=False)
+    B, T, H = case.B, case.T, case.H
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    R = max(1, args.replicas)
+    kv0 = bf16(case.kv_cache)
+    kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    wuk0, wuv0 = bf16(case.w_uk), bf16(case.w_uv)
+    wuk = [wuk0] + [wuk0.clone() for _ in range(R - 1)]
+    wuv = [wuv0] + [wuv0.clone() for _ in range(R - 1)]
+    q_nope, q_pe = bf16(case.q_nope), bf16(case.q_pe)
+    block_table = torch.from_numpy(case.block_table).to(dev)
+    seqlens = torch.from_numpy(case.seqlens).to(dev)
+    max_seqlen = case.max_seqlen
+    scale = mk.softmax_scale()
+
+    S = args.splits
+    buf = mk.DecodeBuffers(B, T, H, max_seqlen, case.page_size, S, dev) if S != 1 else None
+    q_lat = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
+    latent = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(r, ev=None):
+        mk.mla_absorb_q(q_nope, wuk[r], q_lat=q_lat)
+        if ev is not None:
+            ev[0].record(stream)
+        if S == 1:
+            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
+                                 num_splits=1, out_latent=latent, lse=lse)
+        else:
+            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
+                                 num_splits=S, buffers=buf, merge=False)
+        if ev is not None:
+            ev[1].record(stream)
+        if S != 1:
+            mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, B, out_latent=latent,
+                                lse=lse)
+        mk.mla_unabsorb_out(latent, wuv[r], out=out)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms_avg = float(np.mean(dec_ms))
+
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
+        # factor that turns those counters into bytes for the decode kernel
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    dec_bytes, dec_flops = decode_algorithmic(case)
+    achieved = dec_bytes / (dec_ms_avg * 1e-3) / 1e9
+    value = B * T / (ms_per_step * 1e-3)
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "decode_hbm_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            from mla_latent_kv_amd import _build
+            rec = json.load(open(tpath))
+            if rec.get("source_sha256") == _build.kernel_source_hash() and rec.get("workload") == wl.name \
+                    and int(rec.get("splits", -1)) == S:
+                traffic = rec["bytes_per_launch"]
+        except Exception:
+            traffic = None
+
+    result = {
+        "metric": "MLA absorbed decode tokens/s + achieved HBM TB/s (% peak), H=128 B=64 L=4096",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "L": wl.L, "page_size": wl.page_size,
+                   "kv_lora_rank": 512, "rope": 64, "num_splits": S, "cache_replicas": R},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "detail": {
+            "kernel": "decode_kernel (latent attention, split-KV partials)",
+            "decode_us": dec_ms_avg * 1e3,
+            "decode_us_min": float(np.min(dec_ms)) * 1e3,
+            "decode_alg_bytes": dec_bytes,
+            "decode_alg_flops": dec_flops,
+            "decode_tflops": dec_flops / (dec_ms_avg * 1e-3) / 1e12,
+            "decode_mfma_frac": dec_flops / (dec_ms_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "chain_alg_bytes": chain_algorithmic(case, dec_bytes),
+            "chain_TBps": chain_algorithmic(case, dec_bytes) / (ms_per_step * 1e-3) / 1e12,
+        },
+    }
+    if not args.no_cpu:
+        try:
+            threads = min(16, len(os.sched_getaffinity(0)))
+        except AttributeError:
+            threads = min(16, os.cpu_count() or 1)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

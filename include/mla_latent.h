@@ -77,7 +77,7 @@ int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, 
                  int H, int d_nope, int r, void* stream);
 
 /* Sizes the caller must provide for mla_decode_latent with `num_splits`:
- *   *workspace_bytes  -- bytes of the `workspace` argument (0 when num_splits == 1);
+ *   *workspace_bytes  -- bytes of the `workspace` argument (0 unless num_splits == 0);
  *   *max_total_splits -- rows of part_out / part_lse (0 when num_splits == 1).
  * num_splits: 1 = no split; S > 1 = every sequence cut into S chunks (see
  * mla_decode_latent); 0 = automatic (split counts chosen on the device from the
@@ -108,8 +108,9 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
  *               chunks may be empty); chunk s writes its partial state to row
  *               split_indptr[b] + s of part_out / part_lse.
  *               0: automatic split counts (see mla_decode_workspace_size).
- *   workspace   device scratch of the size reported by mla_decode_workspace_size;
- *               may be NULL when num_splits == 1.  Contents on entry are ignored.
+ *   workspace   device scratch of the size reported by mla_decode_workspace_size
+ *               (the automatic mode's work list); may be NULL when that size is 0.
+ *               Contents on entry are ignored.
  *   part_out    [max_total_splits,T,H,r] f32: partial outputs, each divided by its
  *               own softmax denominator (mlxcel Stage 2 contract)
  *   part_lse    [max_total_splits,T,H] f32: natural-log LSE of each partial;
@@ -121,8 +122,9 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
  *               partials are merged on the device before the call returns
  *               (stream order) and out_latent / lse receive the merged result.
  *   lse         [B,T,H] f32 natural-log LSE of each query row; nullable.
- * Returns MLA_ERR_WORKSPACE when num_splits != 1 and workspace, part_out,
- * part_lse or split_indptr is missing or workspace_bytes is too small. */
+ * Returns MLA_ERR_WORKSPACE when num_splits != 1 and part_out, part_lse or
+ * split_indptr is missing, or the workspace is missing or smaller than
+ * mla_decode_workspace_size reports. */
 int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
                       int num_blocks, int page_size, const int32_t* block_table,
                       int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,

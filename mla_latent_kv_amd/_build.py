@@ -57,5 +57,18 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel and ABI sources (identifies which build a stored
+    counter measurement belongs to)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

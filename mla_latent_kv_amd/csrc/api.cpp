@@ -124,7 +124,8 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
     max_items = std::min<long long>((long long)B * kAutoCap, (long long)B + cus);
   }
   if (max_items > (1LL << 30)) return MLA_ERR_SHAPE;
-  *workspace_bytes = plan_bytes(max_items);
+  // only the automatic mode keeps a device work list; uniform splits need none
+  *workspace_bytes = num_splits == 0 ? plan_bytes(max_items) : 0;
   *max_total_splits = (int)max_items;
   return MLA_OK;
 }
@@ -182,37 +183,40 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   if ((st = mla_decode_workspace_size(B, T, H, r, max_seqlen, page_size, num_splits, &need,
                                       &max_items)))
     return st;
-  if (!workspace || !part_out || !part_lse || !split_indptr) return MLA_ERR_WORKSPACE;
-  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  if (!aligned16(workspace) || !aligned16(part_out) || !aligned4(part_lse) || !aligned4(split_indptr))
+  if (!part_out || !part_lse || !split_indptr) return MLA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  if ((workspace && !aligned16(workspace)) || !aligned16(part_out) || !aligned4(part_lse) ||
+      !aligned4(split_indptr))
     return MLA_ERR_ALIGN;
   if (out_latent && !aligned16(out_latent)) return MLA_ERR_ALIGN;
   if ((long long)max_items * n_rg > (1LL << 31) - 1) return MLA_ERR_SHAPE;
 
-  int32_t* n_items = (int32_t*)workspace;
-  int32_t* work = (int32_t*)((char*)workspace + 256);
-  mla::PlanParams pp{};
-  pp.seqlens = seqlens;
-  pp.B = B;
-  pp.num_splits = num_splits;
-  pp.page_size = page_size;
-  pp.min_chunk = kMinChunk;
-  pp.cap = kAutoCap;
-  pp.target_units = 1;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.split_indptr = split_indptr;
+  p.num_splits = num_splits;
   if (num_splits == 0) {
+    // automatic split counts need the lengths: a one-workgroup plan kernel builds
+    // the work list on the device (no host synchronisation)
+    int32_t* n_items = (int32_t*)workspace;
+    int32_t* work = (int32_t*)((char*)workspace + 256);
+    mla::PlanParams pp{};
+    pp.seqlens = seqlens;
+    pp.B = B;
+    pp.num_splits = 0;
+    pp.page_size = page_size;
+    pp.min_chunk = kMinChunk;
+    pp.cap = kAutoCap;
     int cus = 0;
     if ((st = device_cus(&cus))) return st;
     pp.target_units = std::max(1, cus / n_rg);
+    pp.work = work;
+    pp.n_items = n_items;
+    pp.split_indptr = split_indptr;
+    if ((st = launch_status(mla::launch_plan(pp, s)))) return st;
+    p.work = work;
+    p.n_items = n_items;
   }
-  pp.work = work;
-  pp.n_items = n_items;
-  pp.split_indptr = split_indptr;
-  if ((st = launch_status(mla::launch_plan(pp, s)))) return st;
-
-  p.work = work;
-  p.n_items = n_items;
-  p.part_out = part_out;
-  p.part_lse = part_lse;
   if ((st = launch_status(mla::launch_decode(p, max_items * n_rg, true, true, s)))) return st;
   if (out_latent) {
     mla::MergeParams mp{part_out, part_lse, split_indptr, B, T * H, out_latent, lse};

@@ -107,12 +107,27 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   int b, j0, j1, slot;
   if constexpr (SPLIT) {
-    if (item >= *p.n_items) return;
-    const int32_t* wi = p.work + 4 * item;
-    b = wi[0];
-    j0 = wi[1];
-    j1 = wi[2];
-    slot = wi[3];
+    if (p.work) {  // automatic split counts: work list from the plan kernel
+      if (item >= *p.n_items) return;
+      const int32_t* wi = p.work + 4 * item;
+      b = wi[0];
+      j0 = wi[1];
+      j1 = wi[2];
+      slot = wi[3];
+    } else {  // S uniform chunks of ceil(ceil(L/S)/P)*P tokens per sequence
+      const int S = p.num_splits;
+      b = item / S;
+      const int s = item - b * S;
+      const int Lb = p.seqlens[b];
+      const int chunk = (((Lb + S - 1) / S + p.page_size - 1) / p.page_size) * p.page_size;
+      j0 = min(s * chunk, Lb);
+      j1 = min(j0 + chunk, Lb);
+      slot = item;
+      if (s == 0 && rg == 0 && threadIdx.x == 0) {
+        p.split_indptr[b + 1] = (b + 1) * S;
+        if (b == 0) p.split_indptr[0] = 0;
+      }
+    }
   } else {
     b = item;
     j0 = 0;

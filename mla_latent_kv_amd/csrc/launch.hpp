@@ -12,8 +12,10 @@ struct DecodeParams {
   const uint16_t* cache;       // [num_blocks,P,576] bf16
   const int32_t* block_table;  // [B,max_blocks]
   const int32_t* seqlens;      // [B]
-  const int32_t* work;         // split mode: [n][4] = (b, j0, j1, slot)
-  const int32_t* n_items;      // split mode: number of work items (device)
+  const int32_t* work;         // automatic split: [n][4] = (b, j0, j1, slot); NULL = uniform
+  const int32_t* n_items;      // automatic split: number of work items (device)
+  int num_splits;              // uniform split count (work == NULL)
+  int32_t* split_indptr;       // uniform split: written by the decode kernel
   int B, T, H, page_size, max_blocks;
   int n_rg;                    // workgroups per work item (ceil(T*H/128))
   float scale_log2;            // softmax_scale * log2(e)

@@ -96,14 +96,14 @@ def test_decode_validation(lib):
     assert _decode(lib, q_lat=None) == NULL
     assert _decode(lib, kv=P17) == ALIGN
     assert _decode(lib, out=None) == NULL        # unsplit needs out_latent
-    assert _decode(lib, S=4) == WS               # split without workspace
+    assert _decode(lib, S=4) == WS               # split without partial buffers
     need = ctypes.c_size_t(0)
     ms = ctypes.c_int(0)
     assert lib.mla_decode_workspace_size(2, 1, 128, 512, 4096, 64, 4, ctypes.byref(need),
                                          ctypes.byref(ms)) == OK
-    assert ms.value == 8 and need.value >= 8 * 16
-    assert _decode(lib, S=4, ws=P16, wsb=need.value - 1, po=P16, pl=P16, si=P16) == WS
-    assert _decode(lib, S=4, ws=P16, wsb=need.value, po=P16, pl=P16, si=None) == WS
+    assert ms.value == 8 and need.value == 0       # uniform splits keep no work list
+    assert _decode(lib, S=4, po=P16, pl=P16, si=None) == WS
+    assert _decode(lib, S=4, po=P17, pl=P16, si=P16) == ALIGN
     assert _decode(lib, B=0, q_lat=None, out=None) == OK
 
 
