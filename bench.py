@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--splits", type=int, default=4,
                     help="split-KV chunks per sequence (0 = automatic)")
+    ap.add_argument("--partials", choices=["bf16", "f32"], default="bf16",
+                    help="dtype of the split partial outputs")
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--no-cpu", action="store_true")
@@ -132,7 +134,9 @@ def main():
     scale = mk.softmax_scale()
 
     S = args.splits
-    buf = mk.DecodeBuffers(B, T, H, max_seqlen, case.page_size, S, dev) if S != 1 else None
+    part_dtype = torch.bfloat16 if args.partials == "bf16" else torch.float32
+    buf = mk.DecodeBuffers(B, T, H, max_seqlen, case.page_size, S, dev, part_dtype=part_dtype) \
+        if S != 1 else None
     q_lat = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
     latent = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
@@ -194,7 +198,7 @@ def main():
             from mla_latent_kv_amd import _build
             rec = json.load(open(tpath))
             if rec.get("source_sha256") == _build.kernel_source_hash() and rec.get("workload") == wl.name \
-                    and int(rec.get("splits", -1)) == S:
+                    and int(rec.get("splits", -1)) == S and rec.get("partials") == args.partials:
                 traffic = rec["bytes_per_launch"]
         except Exception:
             traffic = None
@@ -213,7 +217,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "L": wl.L, "page_size": wl.page_size,
-                   "kv_lora_rank": 512, "rope": 64, "num_splits": S, "cache_replicas": R},
+                   "kv_lora_rank": 512, "rope": 64, "num_splits": S, "partials": args.partials,
+                   "cache_replicas": R},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "detail": {

@@ -111,8 +111,11 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
  *   workspace   device scratch of the size reported by mla_decode_workspace_size
  *               (the automatic mode's work list); may be NULL when that size is 0.
  *               Contents on entry are ignored.
- *   part_out    [max_total_splits,T,H,r] f32: partial outputs, each divided by its
- *               own softmax denominator (mlxcel Stage 2 contract)
+ *   part_out    [max_total_splits,T,H,r] f32 or bf16 (part_dtype): partial outputs,
+ *               each divided by its own softmax denominator (mlxcel Stage 2
+ *               contract).  bf16 halves the partial traffic; the values are
+ *               convex combinations of cache rows, so their rounding error is
+ *               relative (2^-9) and the merge weights are exact fp32.
  *   part_lse    [max_total_splits,T,H] f32: natural-log LSE of each partial;
  *               -inf for an empty chunk (whose part_out row is zero)
  *   split_indptr [B+1] int32 (out): first partial row of each sequence
@@ -129,21 +132,22 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       int num_blocks, int page_size, const int32_t* block_table,
                       int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
                       int d_R, int max_seqlen, float softmax_scale, int num_splits,
-                      void* workspace, size_t workspace_bytes, float* part_out, float* part_lse,
-                      int32_t* split_indptr, void* out_latent, mla_dtype out_dtype, float* lse,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* part_out,
+                      mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                      void* out_latent, mla_dtype out_dtype, float* lse, void* stream);
 
 /* Merge of split partial states, per (b,t,h) over rows k in
  * [split_indptr[b], split_indptr[b+1]):  M = max_k lse_k, w_k = exp(lse_k - M),
  * lse = M + log(sum_k w_k), out = sum_k w_k * part_out[k] / sum_k w_k.  Rows with
  * lse_k = -inf carry no weight.  Natural-log units only: an LSE in log2 units
  * merges into a plausible but wrong average (mlxcel Stage 2).
- *   part_out [*,T,H,r] f32, part_lse [*,T,H] f32, split_indptr [B+1] int32
+ *   part_out [*,T,H,r] f32 or bf16 (part_dtype), part_lse [*,T,H] f32,
+ *   split_indptr [B+1] int32
  *   out_latent [B,T,H,r] bf16 or f32 (out_dtype), lse [B,T,H] f32 (nullable)
  * Source: M5.8 0x0C (exact merge of (m_r, l_r, o_r); averaging is wrong). */
-int mla_merge_splits(const float* part_out, const float* part_lse, const int32_t* split_indptr,
-                     int B, int T, int H, int r, void* out_latent, mla_dtype out_dtype, float* lse,
-                     void* stream);
+int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* part_lse,
+                     const int32_t* split_indptr, int B, int T, int H, int r, void* out_latent,
+                     mla_dtype out_dtype, float* lse, void* stream);
 
 /* Un-absorb: out[b,t,h,v] = sum_{c<r} latent[b,t,h,c] * W_UV[h,v,c]; latent is
  * rounded to bf16 for the matrix cores when given as f32; fp32 accumulation.

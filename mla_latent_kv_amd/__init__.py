@@ -54,8 +54,8 @@ def load_library():
     L.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, I, P]
     L.mla_decode_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ), ctypes.POINTER(I)]
     L.mla_decode_latent.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I,
-                                    P, SZ, P, P, P, P, I, P, P]
-    L.mla_merge_splits.argtypes = [P, P, P, I, I, I, I, P, I, P, P]
+                                    P, SZ, P, I, P, P, P, I, P, P]
+    L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
@@ -126,14 +126,14 @@ def mla_decode_workspace_size(B, T, H, max_seqlen, page_size, num_splits, r=R_LA
 class DecodeBuffers:
     """Caller-owned scratch of mla_decode_latent in split mode (allocated once, reused)."""
 
-    def __init__(self, B, T, H, max_seqlen, page_size, num_splits, device):
+    def __init__(self, B, T, H, max_seqlen, page_size, num_splits, device, part_dtype=None):
         torch = _torch()
         nbytes, max_splits = mla_decode_workspace_size(B, T, H, max_seqlen, page_size, num_splits)
         self.num_splits = num_splits
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.workspace_bytes = nbytes
-        self.part_out = torch.empty((max(max_splits, 1), T, H, R_LATENT), dtype=torch.float32,
-                                    device=device)
+        self.part_out = torch.empty((max(max_splits, 1), T, H, R_LATENT),
+                                    dtype=part_dtype or torch.float32, device=device)
         self.part_lse = torch.empty((max(max_splits, 1), T, H), dtype=torch.float32, device=device)
         self.split_indptr = torch.empty(B + 1, dtype=torch.int32, device=device)
 
@@ -164,6 +164,7 @@ def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, s
         max_blocks, _ptr(seqlens), B, T, H, r, dr, int(max_seqlen), float(softmax_scale),
         int(num_splits), _ptr(ws), buffers.workspace_bytes if num_splits != 1 else 0,
         _ptr(buffers.part_out if num_splits != 1 else None),
+        _dtype_code(buffers.part_out.dtype) if num_splits != 1 else MLA_F32,
         _ptr(buffers.part_lse if num_splits != 1 else None),
         _ptr(buffers.split_indptr if num_splits != 1 else None),
         _ptr(out_latent if want_out else None), _dtype_code(out_dtype),
@@ -182,8 +183,9 @@ def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=N
         out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=part_out.device)
     if lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=part_out.device)
-    _check(load_library().mla_merge_splits(_ptr(part_out), _ptr(part_lse), _ptr(split_indptr), B, T,
-                                           H, r, _ptr(out_latent), _dtype_code(out_latent.dtype),
+    _check(load_library().mla_merge_splits(_ptr(part_out), _dtype_code(part_out.dtype),
+                                           _ptr(part_lse), _ptr(split_indptr), B, T, H, r,
+                                           _ptr(out_latent), _dtype_code(out_latent.dtype),
                                            _ptr(lse), _stream(stream)), "mla_merge_splits")
     return out_latent, lse
 

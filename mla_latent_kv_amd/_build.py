@@ -18,6 +18,9 @@ HIPCC_FLAGS = [
     # packed fp32 arithmetic is left to nobody: the kernels are compiled without it
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-inline-asm", "-Wno-unused-command-line-argument",
+    # intrinsic MFMAs keep their accumulators in VGPRs; the decode kernel's
+    # 256-register value accumulator is pinned to AGPRs by its inline assembly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

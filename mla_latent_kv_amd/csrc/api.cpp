@@ -134,9 +134,9 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       int num_blocks, int page_size, const int32_t* block_table,
                       int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
                       int d_R, int max_seqlen, float softmax_scale, int num_splits,
-                      void* workspace, size_t workspace_bytes, float* part_out, float* part_lse,
-                      int32_t* split_indptr, void* out_latent, mla_dtype out_dtype, float* lse,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* part_out,
+                      mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                      void* out_latent, mla_dtype out_dtype, float* lse, void* stream) {
   if (B < 0 || num_blocks < 1 || max_blocks_per_seq < 1 || max_seqlen < 0 || num_splits < 0)
     return MLA_ERR_SHAPE;
   int st = check_heads(T, H);
@@ -144,6 +144,7 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   if (r != kR || d_R != kDR) return MLA_ERR_UNSUPPORTED;
   if (page_size < 16 || page_size > 1024 || page_size % 16) return MLA_ERR_UNSUPPORTED;
   if (out_dtype != MLA_BF16 && out_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (part_dtype != MLA_BF16 && part_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MLA_ERR_SHAPE;
   if (B == 0) return MLA_OK;
   if (max_seqlen < T) return MLA_ERR_SHAPE;
@@ -173,7 +174,8 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
     if ((st = check_ptr16(out_latent))) return st;
     p.out = out_latent;
     p.lse = lse;
-    if ((long long)B * n_rg > (1LL << 31) - 1) return MLA_ERR_SHAPE;
+    if ((long long)B * n_rg > (1LL << 31) - 8) return MLA_ERR_SHAPE;
+    p.n_units = B * n_rg;
     return launch_status(mla::launch_decode(p, B * n_rg, false, out_dtype == MLA_F32, s));
   }
 
@@ -189,12 +191,13 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
       !aligned4(split_indptr))
     return MLA_ERR_ALIGN;
   if (out_latent && !aligned16(out_latent)) return MLA_ERR_ALIGN;
-  if ((long long)max_items * n_rg > (1LL << 31) - 1) return MLA_ERR_SHAPE;
+  if ((long long)max_items * n_rg > (1LL << 31) - 8) return MLA_ERR_SHAPE;
 
   p.part_out = part_out;
   p.part_lse = part_lse;
   p.split_indptr = split_indptr;
   p.num_splits = num_splits;
+  p.n_units = max_items * n_rg;
   if (num_splits == 0) {
     // automatic split counts need the lengths: a one-workgroup plan kernel builds
     // the work list on the device (no host synchronisation)
@@ -217,22 +220,24 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
     p.work = work;
     p.n_items = n_items;
   }
-  if ((st = launch_status(mla::launch_decode(p, max_items * n_rg, true, true, s)))) return st;
+  const bool part_f32 = part_dtype == MLA_F32;
+  if ((st = launch_status(mla::launch_decode(p, max_items * n_rg, true, part_f32, s)))) return st;
   if (out_latent) {
     mla::MergeParams mp{part_out, part_lse, split_indptr, B, T * H, out_latent, lse};
-    return launch_status(mla::launch_merge(mp, out_dtype == MLA_F32, s));
+    return launch_status(mla::launch_merge(mp, part_f32, out_dtype == MLA_F32, s));
   }
   return MLA_OK;
 }
 
-int mla_merge_splits(const float* part_out, const float* part_lse, const int32_t* split_indptr,
-                     int B, int T, int H, int r, void* out_latent, mla_dtype out_dtype, float* lse,
-                     void* stream) {
+int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* part_lse,
+                     const int32_t* split_indptr, int B, int T, int H, int r, void* out_latent,
+                     mla_dtype out_dtype, float* lse, void* stream) {
   if (B < 0) return MLA_ERR_SHAPE;
   int st = check_heads(T, H);
   if (st) return st;
   if (r != kR) return MLA_ERR_UNSUPPORTED;
   if (out_dtype != MLA_BF16 && out_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (part_dtype != MLA_BF16 && part_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
   if (B == 0) return MLA_OK;
   if ((st = check_ptr16(part_out)) || (st = check_ptr4(part_lse)) || (st = check_ptr4(split_indptr)) ||
       (st = check_ptr16(out_latent)))
@@ -240,7 +245,8 @@ int mla_merge_splits(const float* part_out, const float* part_lse, const int32_t
   if (lse && !aligned4(lse)) return MLA_ERR_ALIGN;
   if ((long long)B * T * H > (1LL << 31) - 1) return MLA_ERR_SHAPE;
   mla::MergeParams mp{part_out, part_lse, split_indptr, B, T * H, out_latent, lse};
-  return launch_status(mla::launch_merge(mp, out_dtype == MLA_F32, (hipStream_t)stream));
+  return launch_status(
+      mla::launch_merge(mp, part_dtype == MLA_F32, out_dtype == MLA_F32, (hipStream_t)stream));
 }
 
 int mla_validate_inputs(const int32_t* block_table, int max_blocks_per_seq,

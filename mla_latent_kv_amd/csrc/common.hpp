@@ -26,6 +26,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -43,6 +44,12 @@ __device__ __forceinline__ float bf2f(uint16_t h) {
 // two floats -> packed bf16x2 (low = a), nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+// four floats -> four bf16 with the hardware conversion (v_cvt_pk_bf16_f32,
+// round to nearest even), packed two per dword, element 0 in the low half.
+__device__ __forceinline__ u32x2 cvt_bf16x4(f32x4 v) {
+  return __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
 }
 
 // Operands are assembled from whole vectors (bit casts and shuffles), never by
@@ -68,6 +75,16 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
 // LDS reads behind it; the caller orders it with explicit vmcnt waits.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr)
+               : "memory");
+}
+
+// Same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// offset (the instruction's scalar-base form): lane i reads base + voff_i.  The
+// instruction's immediate offset is left at 0: for these loads it displaces
+// the LDS destination as well as the global address.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds_addr)
                : "memory");
 }
 

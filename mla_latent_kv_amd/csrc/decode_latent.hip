@@ -16,30 +16,43 @@
 //
 // Workgroup layout (256 threads = 4 waves of 64, one workgroup per CU):
 //  * KV tiles of 16 tokens (18 KB) stream HBM -> LDS with direct-to-LDS loads
-//    into a ring of NB buffers, NB-1 tiles ahead of use.  Every wave issues a
-//    quarter of each tile's 18 load instructions.
+//    into a ring of NB buffers.  Every wave issues a quarter of each tile's 18
+//    load instructions.
 //  * Score phase: wave w owns query rows [32w, 32w+32) and computes
 //    S^T[16 tok x 32 rows] with 16x16x32 MFMAs; the K operand is read from LDS
 //    with ds_read_b128, the query lives in registers for the whole kernel.
 //  * Softmax: log2 domain against a per-row reference m_ref (the max of the
 //    row's first tile with a visible key), so exponentials are bounded by
-//    2^kLazy; the fp32 accumulator is never rescaled.  If a later tile's max
-//    exceeds m_ref by more than kLazy, m_ref is raised and the work unit is
-//    replayed from its first tile (exact for any finite scores; not taken for
-//    scores of ordinary magnitude).
-//  * Probabilities (bf16) of all 128 rows are exchanged through LDS.
+//    2^kLazy and the fp32 accumulator is never rescaled.  Each lane checks its
+//    own scores against m_ref + kLazy; only when one exceeds it is the row max
+//    reduced across lanes, m_ref raised and the work unit replayed from its
+//    first tile (exact for any finite scores; never taken for scores of
+//    ordinary magnitude).
+//  * Probabilities (bf16) of all 128 rows are exchanged through LDS (two
+//    buffers, alternating tiles).
 //  * Value phase: wave w owns latent columns [128w, 128w+128) of all 128 rows
 //    (O^T accumulator 128 x 128 fp32 = 256 registers) and multiplies
 //    V^T[32 cols x 16 tok] (transposing LDS reads) by P^T[16 tok x 32 rows]
 //    with 32x32x16 MFMAs.  Splitting the value GEMM by columns rather than by
 //    rows means each V element is read from LDS once per workgroup instead of
 //    once per wave.
+//  * Software pipeline, one barrier per tile: after the barrier of step i the
+//    wave computes the scores of tile i+1, then issues the value MFMAs of tile
+//    i with the softmax of tile i+1 placed between them, so the vector ALU
+//    work runs while the matrix core is busy.
 //
 // Tile LDS layout (chunk-major): the 16-byte chunk c (c < 72) of tile row t is
-// stored at chunk position 16c + (t ^ 4(c & 1)).  A K read (16 rows of one
-// chunk) is then 256 contiguous bytes, a transposing V read (4 rows x 2
-// adjacent chunks per 16 lanes) touches 32 distinct banks, and every address
-// is one per-lane base plus an immediate offset.
+// stored at chunk position 16c + (t ^ g(c & 3)) with g = (0, 12, 8, 4).  A K
+// read (16 rows of 4 chunks) and a transposing V read are then both free of
+// bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT; g = (0, 4, 8,
+// 12), the obvious choice, makes the 16-byte K reads conflict 2-way); the
+// direct-to-LDS loads write 1 KB contiguous.
+//
+// Probability buffer: row R (of 128) holds 16 bf16 = two 16-byte chunks, chunk c
+// (tokens 8c..8c+7) at byte 32R + 16(c ^ s(R)), s(R) = ((R >> 2) ^ (R >> 4)) & 1;
+// 16-byte writes and reads of it are conflict-free.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -47,10 +60,25 @@ namespace mla {
 
 constexpr float kLazy = 64.0f;  // log2-domain growth of the max tolerated before a replay
 
-
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `tiles` of this wave's most recent tile loads are in
+// flight (PER = load instructions per tile issued by this wave).
+template <int PER, int MAXT>
+__device__ __forceinline__ void wait_tiles(int tiles) {
+  static_assert(MAXT <= 6, "extend the switch");
+  switch (tiles < MAXT ? tiles : MAXT) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<PER>(); break;
+    case 2: wait_vm<2 * PER>(); break;
+    case 3: if constexpr (MAXT >= 3) wait_vm<3 * PER>(); break;
+    case 4: if constexpr (MAXT >= 4) wait_vm<4 * PER>(); break;
+    case 5: if constexpr (MAXT >= 5) wait_vm<5 * PER>(); break;
+    default: if constexpr (MAXT >= 6) wait_vm<6 * PER>(); break;
+  }
 }
 
 // Cross-lane pair exchange.  v_permlane16_swap exchanges the odd 16-lane rows of
@@ -83,6 +111,15 @@ __device__ __forceinline__ float sum4lanes(float v) {
   return a + b;
 }
 
+// max of four floats in two VALU ops (v_max3 does not canonicalise its inputs;
+// the scores here are never signalling NaNs)
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_max3_f32 %0, %1, %2, %2" : "=v"(r) : "v"(r), "v"(d));
+  return r;
+}
+
 __device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr;
 }
@@ -91,24 +128,61 @@ __device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
 __device__ __forceinline__ s16x4 lds_tr16(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)addr);
 }
+__device__ __forceinline__ void lds_st64(uint32_t addr, u32x2 v) {
+  *(__attribute__((address_space(3))) u32x2*)(uintptr_t)addr = v;
+}
+
+// Value-phase MFMA with its accumulator pinned to AGPRs (the 128x128 fp32 O^T
+// block of a wave fills all 256 of them); written as inline assembly so that
+// the score accumulators, which the softmax reads, stay in VGPRs.  The operands
+// come straight from LDS reads (the compiler's wait counts cover them); the
+// accumulator is next touched by VALU code only after mfma_drain().
+__device__ __forceinline__ void mfma_pv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last value MFMA and any VALU access to its
+// accumulator (a 16-pass XDL result needs at most 18).
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// Row swizzle of the tile layout and the position (in 16-byte units) of chunk c
+// of tile row t.
+__device__ __forceinline__ int tile_swz(int c) { return (-4 * c) & 12; }
+__device__ __forceinline__ int tile_pos(int c, int t) { return 16 * c + (t ^ tile_swz(c & 3)); }
+// probability-buffer chunk swap of row r
+__device__ __forceinline__ int pbuf_swz(int r) { return ((r >> 2) ^ (r >> 4)) & 1; }
+// v_permlane16_swap of two different registers: afterwards a = [a.r0, b.r0,
+// a.r2, b.r2] and b = [a.r1, b.r1, a.r3, b.r3] (r = 16-lane row)
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 
 template <int NB, bool SPLIT, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[NB * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[kRowsPerWG * kTile];
+  // tile ring; after the last tile it is reused to stage the 128 KB output block
+  constexpr int kRingBytes = NB * kTileBytes > 128 * 1024 ? NB * kTileBytes : 128 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kRingBytes];
+  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2 * kRowsPerWG * kTile];
   __shared__ __attribute__((aligned(16))) float inv_s[kRowsPerWG];
-  __shared__ __attribute__((aligned(16))) unsigned flag_s[4];
+  __shared__ unsigned flag_s;
 
   const int w = wave_id();
   const int l = lane_id();
-  const int wg = blockIdx.x;
-  const int item = wg / p.n_rg;
-  const int rg = wg - item * p.n_rg;
+
+  // ---- work unit.  Units u = item * n_rg + rg are dealt to the XCDs in
+  // contiguous ranges (workgroup i runs on XCD i % 8), so the splits of one
+  // sequence share an L2 and re-read its query rows from there.
+  const int n_units = (SPLIT && p.work) ? *p.n_items * p.n_rg : p.n_units;
+  const int per_xcd = (n_units + 7) >> 3;
+  const int kx = blockIdx.x >> 3;
+  if (kx >= per_xcd) return;
+  const int u = (blockIdx.x & 7) * per_xcd + kx;
+  if (u >= n_units) return;
+  const int item = u / p.n_rg;
+  const int rg = u - item * p.n_rg;
 
   int b, j0, j1, slot;
   if constexpr (SPLIT) {
     if (p.work) {  // automatic split counts: work list from the plan kernel
-      if (item >= *p.n_items) return;
       const int32_t* wi = p.work + 4 * item;
       b = wi[0];
       j0 = wi[1];
@@ -134,21 +208,30 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     j1 = p.seqlens[b];
     slot = b;
   }
-  const int L = p.seqlens[b];
+  // work-unit scalars are wave-uniform: keep them in scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  j0 = __builtin_amdgcn_readfirstlane(j0);
+  j1 = __builtin_amdgcn_readfirstlane(j1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  const int L = __builtin_amdgcn_readfirstlane(p.seqlens[b]);
   const int T = p.T, H = p.H, TH = T * H;
   const int P = p.page_size;
   const int row0 = rg * kRowsPerWG;
 
   // ---- query rows of this wave (score phase) and their visible limits ----
+  // dd[nb] = (first invisible key of the row) - j0 - 4(l>>4): key r of the lane's
+  // 4-key group in tile i is visible iff r < dd[nb] - 16 i.  Padding rows past
+  // T*H get a zero query and see every key (their scores are 0, never stored).
   bf16x8 q[2][18];
-  int lim[2];
+  int dd[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int gr = row0 + 32 * w + 16 * nb + (l & 15);
+    int lim = j1;
     if (gr < TH) {
       const int t = gr / H;
       const int h = gr - t * H;
-      lim[nb] = min(L - T + t + 1, j1);
+      lim = min(L - T + t + 1, j1);
       const uint16_t* ql = p.q_lat + ((size_t)(b * T + t) * H + h) * kR + 8 * (l >> 4);
       const uint16_t* qp = p.q_pe + ((size_t)(b * T + t) * H + h) * kDR + 8 * (l >> 4);
 #pragma unroll
@@ -156,10 +239,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) q[nb][16 + ks] = *(const bf16x8*)(qp + 32 * ks);
     } else {
-      lim[nb] = j0;  // padded row: nothing visible
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) q[nb][ks] = bf16x8{};
     }
+    dd[nb] = lim - j0 - 4 * (l >> 4);
   }
 
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
@@ -174,6 +257,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     const int pg = pg_base + l;
     if (pg < p.max_blocks && pg * P < j1) pg_vec = bt_row[pg];
   }
+  if (threadIdx.x == 0) flag_s = 0u;
   // q and the first page ids must be complete before any tile load is in flight:
   // this wait is visible to the compiler, so it does not later wait for them
   // against the (compiler-invisible) tile loads.
@@ -181,170 +265,332 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   // Load tile `it` into ring buffer it % NB: this wave issues instructions
   // k = w, w+4, ... of the tile's 18; instruction k fills chunk positions
-  // [64k, 64k+64), i.e. chunks 4k .. 4k+3 of all 16 rows.  Lane l brings chunk
-  // 4k + (l>>4) of row (l & 15) ^ 4((l>>4) & 1).
-  const uint32_t dma_lane = (((l & 15) ^ (4 * ((l >> 4) & 1))) * kRowChunks + (l >> 4)) * 16;
-  auto issue = [&](int it) {
+  // [64k, 64k+64), i.e. chunks 4k .. 4k+3 of all 16 rows.  Lane l writes
+  // position 64k + l: chunk 4k + (l>>4) of row (l & 15) ^ g(l>>4).
+  const uint32_t dma_lane = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4);
+  // Tile loads are issued a few instructions at a time between the MFMAs:
+  // issue_prep(it) selects tile `it` (its page and ring buffer), issue_part(n)
+  // issues this wave's n-th load instruction of it (k = w + 4n < 18).  The
+  // tile's global base is wave-uniform (scalar registers); lane offsets are
+  // dma_lane + 64w + 256n.
+  const uint32_t dma_voff = dma_lane + 64 * w;
+  const uint8_t* dma_base = cache;
+  uint32_t dma_dst = 0;
+  auto issue_prep = [&](int it) {
     const int jt = j0 + it * kTile;
     const int page = jt / P;
     if (page >= pg_base + 64) {
       pg_base += 64;
       const int pg = pg_base + l;
       pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
+      // complete the reload here, visibly to the compiler, so that the common
+      // path carries no wait for it (a vector-memory wait would also drain the
+      // in-flight tile loads)
+      __builtin_amdgcn_s_waitcnt(0);
     }
     const int phys = __builtin_amdgcn_readlane(pg_vec, page - pg_base);
-    const uint8_t* tb = cache + ((size_t)phys * P + (jt - page * P)) * kRowBytes + dma_lane;
-    const uint32_t lb = tiles_lds + (it % NB) * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      const int k = w + 4 * i;
-      if (k < 18) dma16(tb + 64 * k, lb + k * 1024);
+    dma_base = cache + ((size_t)phys * P + (jt - page * P)) * kRowBytes;
+    dma_dst = tiles_lds + (it % NB) * kTileBytes + 1024 * w;
+  };
+  auto issue_part = [&](auto n_const) {
+    constexpr int n = decltype(n_const)::value;
+    if (w + 4 * n < 18) dma16s(dma_voff + 256 * n, dma_base, dma_dst + 4096 * n);
+  };
+  auto issue = [&](int it) {
+    issue_prep(it);
+    issue_part(std::integral_constant<int, 0>{});
+    issue_part(std::integral_constant<int, 1>{});
+    issue_part(std::integral_constant<int, 2>{});
+    issue_part(std::integral_constant<int, 3>{});
+    issue_part(std::integral_constant<int, 4>{});
+  };
+  // Rows past the end of the range were loaded from the rest of the page, which
+  // may hold anything: clear their value chunks so that 0-probability x row is 0.
+  auto clear_tail = [&](int it) {
+    const int nvalid = j1 - (j0 + it * kTile);
+    if (nvalid >= kTile) return;
+    const uint32_t buf = tiles_lds + (it % NB) * kTileBytes;
+    for (int x = threadIdx.x; x < 64 * kTile; x += 256) {
+      const int c = x >> 4, t = x & 15;
+      if (t >= nvalid)
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(buf + tile_pos(c, t) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
   // score-phase K reads: lane reads chunk 4ks + (l>>4) of tile row (l & 15)
-  const uint32_t k_lane = (((l >> 4) * 16) + ((l & 15) ^ (4 * ((l >> 4) & 1)))) * 16;
-  // value-phase transposing reads: group g = l>>4, lane j = l&15; read r covers rows
-  // 8(g>>1) + 4r + (j>>2) and columns 32fb + 16(g&1) + 4(j&3) .. +3, i.e. chunk
-  // 4fb + 2(g&1) + ((j>>1)&1), byte 8(j&1) of the chunk
+  const uint32_t k_lane = ((l >> 4) * 16 + ((l & 15) ^ tile_swz(l >> 4))) * 16;
+  // value-phase transposing reads: group g = l>>4, lane j = l&15; read r covers
+  // rows 8(g>>1) + 4r + (j>>2) and columns 32fb + 16(g&1) + 4(j&3) .. +3, i.e.
+  // chunk 4fb + cl with cl = 2(g&1) + ((j>>1)&1), byte 8(j&1) of the chunk
   uint32_t v_lane[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int g = l >> 4, j = l & 15;
     const int tok = 8 * (g >> 1) + 4 * r + (j >> 2);
     const int cl = 2 * (g & 1) + ((j >> 1) & 1);
-    v_lane[r] = (cl * 16 + (tok ^ (4 * (cl & 1)))) * 16 + 8 * (j & 1);
+    v_lane[r] = (16 * cl + (tok ^ tile_swz(cl))) * 16 + 8 * (j & 1);
   }
+  // probability buffer: after the row exchange in sm_store lane l holds tokens
+  // 8(l>>5) .. +7 of row 32w + (l & 31); the value phase reads row 32rb + (l & 31),
+  // chunk l>>5 (the P^T operand layout)
   const uint32_t pbuf_lds = lds_addr_of(pbuf);
-  const uint32_t flag_lds = lds_addr_of(flag_s);
+  const uint32_t p_rd = (l & 31) * 32 + 16 * ((l >> 5) ^ pbuf_swz(l & 31));
+  const uint32_t p_wr = 32 * 32 * w + p_rd;
   const float sl2 = p.scale_log2;
+  const float lazy_raw = kLazy / sl2;
 
-  // Softmax reference per row: the max of the row's first tile with a visible key.
-  // Probabilities are exp2(s - m_ref).  A tile whose max exceeds m_ref by more
-  // than kLazy raises m_ref; the pass is then finished and replayed from the
-  // first tile (exact for any finite scores; never taken for scores of O(1)).
+  // Per-row softmax reference (log2 domain) and the raw-score threshold above
+  // which a replay is needed; nmb = -m_ref (0 while the row has no visible key).
   float m_ref[2] = {-INFINITY, -INFINITY};
+  float nmb[2] = {0.f, 0.f};
+  float thr[2] = {INFINITY, INFINITY};
+  bool ref_pending = true;
   float l_part[2];
   f32x16 acc[4][4];
-  for (;;) {
+
+  // ---- softmax pieces of one tile (scores s0, s1 of tile `it`) ----
+  float x[2][4], mxl[2];
+  float (&pr)[2][4] = x;  // probabilities overwrite the masked scores
+  bool grow = false;
+  auto sm_mask = [&](int nb, const f32x4& s, int it) {
+    const int rel = dd[nb] - kTile * it;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[nb][r] = (r < rel) ? s[r] : -INFINITY;
+  };
+  auto sm_check = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mxl[nb] = max4(x[nb][0], x[nb][1], x[nb][2], x[nb][3]);
+    grow = __builtin_amdgcn_ballot_w64((mxl[0] > thr[0]) | (mxl[1] > thr[1])) != 0;
+  };
+  auto sm_reference = [&]() {  // first visible tile of a row: fix m_ref
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float mx = max4lanes(max4(x[nb][0], x[nb][1], x[nb][2], x[nb][3]));
+      if (m_ref[nb] == -INFINITY && mx != -INFINITY) {
+        m_ref[nb] = mx * sl2;
+        nmb[nb] = -m_ref[nb];
+        thr[nb] = mx + lazy_raw;
+      }
+    }
+    ref_pending = __builtin_amdgcn_ballot_w64((m_ref[0] == -INFINITY) | (m_ref[1] == -INFINITY)) != 0;
+  };
+  auto sm_fma = [&](int nb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[nb][r] = __builtin_fmaf(x[nb][r], sl2, nmb[nb]);
+  };
+  auto sm_exp = [&](int nb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[nb][r] = __builtin_amdgcn_exp2f(pr[nb][r]);
+  };
+  auto sm_sum = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) l_part[nb] += (pr[nb][0] + pr[nb][1]) + (pr[nb][2] + pr[nb][3]);
+  };
+  // Probabilities to bf16, then one row exchange turns the score layout (lane:
+  // row (l&15) + 16nb, tokens 4(l>>4)..+3) into 8 consecutive tokens of one row
+  // per lane (row l & 31, tokens 8(l>>5)..+7), stored with one 16-byte write.
+  auto sm_store = [&](int it) {
+    const uint32_t base = pbuf_lds + (it & 1) * (kRowsPerWG * kTile * 2);
+    u32x2 a = cvt_bf16x4(f32x4{pr[0][0], pr[0][1], pr[0][2], pr[0][3]});
+    u32x2 c = cvt_bf16x4(f32x4{pr[1][0], pr[1][1], pr[1][2], pr[1][3]});
+    uint32_t a0 = a[0], a1 = a[1], c0 = c[0], c1 = c[1];
+    swap16(a0, c0);
+    swap16(a1, c1);
+    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + p_wr) = u32x4{a0, a1, c0, c1};
+  };
+  // a row's max grew by more than kLazy: raise its reference, flag a replay
+  auto sm_grow = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float mx = max4lanes(mxl[nb]);
+      if (mx > thr[nb]) {
+        m_ref[nb] = mx * sl2;
+        nmb[nb] = -m_ref[nb];
+        thr[nb] = mx + lazy_raw;
+      }
+    }
+    if (l == 0) flag_s = 1u;
+  };
+  // whole softmax of one tile, not interleaved (first tile, rows still without
+  // a reference)
+  auto softmax_tile = [&](const f32x4& s0, const f32x4& s1, int it) {
+    sm_mask(0, s0, it);
+    sm_mask(1, s1, it);
+    if (ref_pending) sm_reference();
+    sm_check();
+    sm_fma(0);
+    sm_fma(1);
+    sm_exp(0);
+    sm_exp(1);
+    sm_sum();
+    sm_store(it);
+    if (grow) sm_grow();
+  };
+
+  // scores S^T of tile `it` (not interleaved: prologue)
+  auto scores_plain = [&](int it, f32x4& s0, f32x4& s1) {
+    const uint32_t kbase = tiles_lds + (it % NB) * kTileBytes + k_lane;
+    s0 = f32x4{};
+    s1 = f32x4{};
+    constexpr int PF = 4;
+    bf16x8 kb[PF];
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const bf16x8 kop = kb[ks % PF];
+      if (ks + PF < 18) kb[ks % PF] = lds_b128(kbase + 1024 * (ks + PF));
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], s1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Smallest key limit over this wave's rows: a tile ending at or before it
+  // needs no mask for any of them.
+  int lim_lo = j1;
+  {
+    const int g0 = row0 + 32 * w;
+    if (g0 < TH) lim_lo = min(L - T + g0 / H + 1, j1);
+  }
+
+  // At most one replay: after a flagged pass every row's reference is within
+  // kLazy of its true maximum, so the replay cannot flag again.
+  for (int pass = 0;; ++pass) {
     if (pg_base != j0 / P) {  // a replay after the page window moved: rewind it
       pg_base = j0 / P;
       const int pg = pg_base + l;
       pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
+      __builtin_amdgcn_s_waitcnt(0);
     }
     l_part[0] = l_part[1] = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int xx = 0; xx < 4; ++xx)
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = f32x16{};
+      for (int y = 0; y < 4; ++y) acc[xx][y] = f32x16{};
     for (int it = 0; it < NB - 1 && it < ntiles; ++it) issue(it);
-    bool replay = false;
-    for (int i = 0; i < ntiles; ++i) {
-      // tile i has landed once at most NB-2 later tiles of this wave's loads are in flight
-      if (i + NB - 2 < ntiles) {
-        if (w < 2) wait_vm<5 * (NB - 2)>();
-        else wait_vm<4 * (NB - 2)>();
-      } else {
-        wait_vm<0>();
-      }
+
+    // Two-stage pipeline.  Step i (after its barrier): value MFMAs of tile i
+    // (probabilities P(i) written during step i-1), score MFMAs of tile i+2,
+    // and the softmax of tile i+1 (scores from step i-1) producing P(i+1).
+    // Resident ring buffers: tiles i, i+1, i+2; up to NB-4 more in flight.
+    f32x4 s0 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, s1 = s0;  // scores of tile i+1
+    if (ntiles > 0) {
+      // prologue: tiles 0 and 1 landed; P(0) and the scores of tile 1
+      const int ahead = max(0, min(NB - 1, ntiles) - 2);
+      if (w < 2) wait_tiles<5, NB - 3>(ahead);
+      else wait_tiles<4, NB - 3>(ahead);
       barrier();
-      if (i + NB - 1 < ntiles) issue(i + NB - 1);
-      const uint32_t buf = tiles_lds + (i % NB) * kTileBytes;
-      const int nvalid = j1 - (j0 + i * kTile);
-      if (nvalid < kTile) {
-        // Rows past the end of the range were loaded from the rest of the page,
-        // which may hold anything: clear them so that 0-probability x row stays 0.
-        for (int x = threadIdx.x; x < kRowChunks * kTile; x += 256) {
-          const int c = x >> 4, t = x & 15;
-          if (t >= nvalid)
-            *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(buf + (c * 16 + (t ^ (4 * (c & 1)))) * 16) =
-                u32x4{0u, 0u, 0u, 0u};
-        }
-        wait_lgkm0();
-        barrier();
-      }
-
-      // ---- scores: S^T[16 tok x 32 rows], K operand reads 4 steps ahead ----
-      f32x4 s0 = {}, s1 = {};
-      {
-        constexpr int PF = 4;
-        bf16x8 kb[PF];
-#pragma unroll
-        for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(buf + k_lane + 1024 * ks);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const bf16x8 kop = kb[ks % PF];
-          if (ks + PF < 18)
-            kb[ks % PF] = lds_b128(buf + k_lane + 1024 * (ks + PF));
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], s1, 0, 0, 0);
-          // keep the read of step ks+PF ahead of these MFMAs (no code motion across)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- mask, scale (log2 domain), probabilities ----
-      const int jl = j0 + i * kTile + 4 * (l >> 4);
-      float sv[2][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[0][r] = (jl + r < lim[0]) ? s0[r] * sl2 : -INFINITY;
-        sv[1][r] = (jl + r < lim[1]) ? s1[r] * sl2 : -INFINITY;
-      }
-      bool grow = false;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = fmaxf(fmaxf(sv[nb][0], sv[nb][1]), fmaxf(sv[nb][2], sv[nb][3]));
-        mx = max4lanes(mx);
-        if (m_ref[nb] == -INFINITY) {
-          m_ref[nb] = mx;
-        } else if (mx > m_ref[nb] + kLazy) {
-          m_ref[nb] = mx;
-          grow = true;
-        }
-        const float mb = (m_ref[nb] == -INFINITY) ? 0.f : m_ref[nb];
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[nb][r] - mb);
-        l_part[nb] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        u32x2 pk;
-        pk[0] = pack_bf16x2(pr[0], pr[1]);
-        pk[1] = pack_bf16x2(pr[2], pr[3]);
-        const int row = 32 * w + 16 * nb + (l & 15);
-        *(__attribute__((address_space(3))) u32x2*)(uintptr_t)(pbuf_lds + row * 32 + (l >> 4) * 8) = pk;
-      }
-      const bool any = __builtin_amdgcn_ballot_w64(grow) != 0;
-      if (l == 0) flag_s[w] = any ? 1u : 0u;
-      wait_lgkm0();
-      barrier();
-      const u32x4 fl = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)flag_lds;
-      // a flagged pass is finished (its result is discarded) and then replayed
-      replay |= (fl[0] | fl[1] | fl[2] | fl[3]) != 0u;
-
-      // ---- values: O^T[128 cols x 128 rows] += V^T P^T, next V operand read ahead ----
-      bf16x8 pb[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        pb[rb] = lds_b128(pbuf_lds + (32 * rb + (l & 31)) * 32 + (l >> 5) * 16);
-      bf16x8 vop[2];
-#pragma unroll
-      for (int fbl = 0; fbl < 4; ++fbl) {
-        const int fb = 4 * w + fbl;
-        if (fbl == 0)
-          vop[0] = join8(lds_tr16(buf + v_lane[0] + 1024 * fb), lds_tr16(buf + v_lane[1] + 1024 * fb));
-        __builtin_amdgcn_sched_barrier(0);
-        if (fbl < 3)
-          vop[(fbl + 1) & 1] = join8(lds_tr16(buf + v_lane[0] + 1024 * (fb + 1)),
-                                     lds_tr16(buf + v_lane[1] + 1024 * (fb + 1)));
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[fbl][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[fbl & 1], pb[rb], acc[fbl][rb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      clear_tail(0);
+      if (ntiles > 1) clear_tail(1);
+      f32x4 t0, t1;
+      scores_plain(0, t0, t1);
+      softmax_tile(t0, t1, 0);
+      if (ntiles > 1) scores_plain(1, s0, s1);
     }
-    if (!replay) break;
-    wait_vm<0>();
+    for (int i = 0; i < ntiles; ++i) {
+      const bool do_qk = i + 2 < ntiles;
+      const bool do_sm = i + 1 < ntiles;
+      const bool do_issue = i + NB - 1 < ntiles;
+      // tile i+2 must have landed; up to NB-4 later tiles may stay in flight
+      if (do_qk) {
+        if (w < 2) wait_tiles<5, NB - 4>(min(NB - 4, ntiles - i - 3));
+        else wait_tiles<4, NB - 4>(min(NB - 4, ntiles - i - 3));
+      }
+      wait_lgkm0();  // this wave's probability writes and tail clears
+      barrier();
+      if (do_qk) clear_tail(i + 2);
+      if (do_issue) issue_prep(i + NB - 1);
+
+      // softmax of tile i+1 done up front when some row still needs its
+      // reference; the interleaved copy below then runs on -inf scores, which
+      // makes every one of its steps a no-op (its probabilities are not stored)
+      bool sm_here = do_sm;
+      if (do_sm && ref_pending) {
+        softmax_tile(s0, s1, i + 1);
+        sm_here = false;
+        s0 = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        s1 = s0;
+      }
+      const bool full = j0 + kTile * (i + 2) <= lim_lo;  // tile i+1 needs no mask
+
+      const uint32_t kbase = tiles_lds + ((i + 2) % NB) * kTileBytes + k_lane;
+      const uint32_t pbase = pbuf_lds + (i & 1) * (kRowsPerWG * kTile * 2) + p_rd;
+      const uint32_t vbuf = tiles_lds + (i % NB) * kTileBytes + 4096 * w;
+      const uint32_t vb0 = vbuf + v_lane[0], vb1 = vbuf + v_lane[1];
+      bf16x8 pb[4], vop[2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pb[m] = lds_b128(pbase + 1024 * m);
+      vop[0] = join8(lds_tr16(vb0), lds_tr16(vb1));
+      // (the score MFMAs also run in the last two steps, on a stale buffer; their
+      // results are discarded)
+      constexpr int PF = 4;
+      bf16x8 kb[PF];
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
+      f32x4 n0 = {}, n1 = {};  // scores of tile i+2
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        {
+          const bf16x8 kop = kb[ks % PF];
+          if (ks + PF < 18) kb[ks % PF] = lds_b128(kbase + 1024 * (ks + PF));
+          n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], n0, 0, 0, 0);
+          n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], n1, 0, 0, 0);
+        }
+        if (ks >= 1 && ks <= 16) {
+          const int v = ks - 1, f = v >> 2, rb = v & 3;
+          mfma_pv(acc[f][rb], vop[f & 1], pb[rb]);
+        }
+        // V operand of column block f+1 read a block ahead (two alternating slots)
+        if (ks == 1 || ks == 5 || ks == 9) {
+          const int f = (ks >> 2) + 1;
+          vop[f & 1] = join8(lds_tr16(vb0 + 1024 * f), lds_tr16(vb1 + 1024 * f));
+        }
+        {
+          if (ks == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[0][r] = s0[r];
+            if (!full) sm_mask(0, s0, i + 1);
+          }
+          if (ks == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[1][r] = s1[r];
+            if (!full) sm_mask(1, s1, i + 1);
+          }
+          if (ks == 2) sm_check();
+          if (ks == 3) sm_fma(0);
+          if (ks == 4) { pr[0][0] = __builtin_amdgcn_exp2f(pr[0][0]); pr[0][1] = __builtin_amdgcn_exp2f(pr[0][1]); }
+          if (ks == 5) { pr[0][2] = __builtin_amdgcn_exp2f(pr[0][2]); pr[0][3] = __builtin_amdgcn_exp2f(pr[0][3]); }
+          if (ks == 6) sm_fma(1);
+          if (ks == 7) { pr[1][0] = __builtin_amdgcn_exp2f(pr[1][0]); pr[1][1] = __builtin_amdgcn_exp2f(pr[1][1]); }
+          if (ks == 8) { pr[1][2] = __builtin_amdgcn_exp2f(pr[1][2]); pr[1][3] = __builtin_amdgcn_exp2f(pr[1][3]); }
+          if (ks == 9) sm_sum();
+          if (ks == 10 && sm_here) sm_store(i + 1);
+        }
+        if (do_issue) {
+          if (ks == 2) issue_part(std::integral_constant<int, 0>{});
+          if (ks == 6) issue_part(std::integral_constant<int, 1>{});
+          if (ks == 10) issue_part(std::integral_constant<int, 2>{});
+          if (ks == 14) issue_part(std::integral_constant<int, 3>{});
+          if (ks == 17) issue_part(std::integral_constant<int, 4>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (grow) sm_grow();
+      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      s0 = do_qk ? n0 : ninf;
+      s1 = do_qk ? n1 : ninf;
+    }
+    mfma_drain();
+    wait_lgkm0();
     barrier();
+    const bool replay = flag_s != 0u && pass == 0;
+    if (!replay) break;
+    // a flagged pass is discarded and replayed with the raised references
+    wait_vm0();
+    barrier();
+    if (threadIdx.x == 0) flag_s = 0u;
+    wait_lgkm0();
   }
 
   // ---- finalize: row sums, lse, normalisation ----
@@ -370,33 +616,57 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   }
   wait_lgkm0();
   barrier();
+
+  // ---- store: the workgroup's rows [row0, row0 + 128) of its output are one
+  // contiguous block (1 KB per row in bf16, 2 KB in fp32).  The normalised
+  // accumulators are staged through the (now idle) tile ring in row-major
+  // order, then written with 16-byte-per-lane contiguous stores.  Staging
+  // swizzle: 16-byte chunk c of staged row r sits at chunk c ^ (r & 15); in the
+  // bf16 layout the two 8-byte halves of a chunk are also swapped when bit 4 of
+  // r is set (both make the staging writes and the reads conflict-free).
+  const int n_rows = min(kRowsPerWG, TH - row0);
+  char* const dst_base = (char*)(SPLIT ? p.part_out : p.out) + ((size_t)slot * TH + row0) * kR * (OUT_F32 ? 4 : 2);
+  constexpr int kRowOut = kR * (OUT_F32 ? 4 : 2);      // bytes per output row
+  constexpr int kStageRows = OUT_F32 ? 64 : 128;       // rows per staging round (128 KB)
+  static_assert(kStageRows * kRowOut <= kRingBytes, "staging block exceeds the tile ring");
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int rl = 32 * rb + (l & 31);
-    const int gr = row0 + rl;
-    if (gr >= TH) continue;
-    const float inv = inv_s[rl];
-    const size_t orow = (size_t)(SPLIT ? slot : b) * TH + gr;
+  for (int half = 0; half < 128 / kStageRows; ++half) {
 #pragma unroll
-    for (int fbl = 0; fbl < 4; ++fbl) {
-      const int colb = 128 * w + 32 * fbl + 4 * (l >> 5);
+    for (int rbl = 0; rbl < kStageRows / 32; ++rbl) {
+      const int rb = half * (kStageRows / 32) + rbl;
+      const int r = 32 * rbl + (l & 31);  // staged row
+      const float inv = inv_s[32 * rb + (l & 31)];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int col = colb + 8 * q4;
-        f32x4 v;
+      for (int fbl = 0; fbl < 4; ++fbl) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[fbl][rb][4 * q4 + e] * inv;
-        if constexpr (SPLIT || OUT_F32) {
-          float* dst = (SPLIT ? p.part_out : (float*)p.out) + orow * kR + col;
-          *(f32x4*)dst = v;
-        } else {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(v[0], v[1]);
-          pk[1] = pack_bf16x2(v[2], v[3]);
-          *(u32x2*)((uint16_t*)p.out + orow * kR + col) = pk;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[fbl][rb][4 * q4 + e] * inv;
+          // columns 128w + 32fbl + 8q4 + 4(l>>5) + [0,4)
+          if constexpr (OUT_F32) {
+            const int c = 32 * w + 8 * fbl + 2 * q4 + (l >> 5);
+            *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16)) = v;
+          } else {
+            const int c = 16 * w + 4 * fbl + q4;
+            const int hh = (l >> 5) ^ ((r >> 4) & 1);
+            lds_st64(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16) + 8 * hh, cvt_bf16x4(v));
+          }
         }
       }
     }
+    wait_lgkm0();
+    barrier();
+    const int rows_here = min(kStageRows, n_rows - half * kStageRows);
+    char* const dst = dst_base + (size_t)half * kStageRows * kRowOut;
+    constexpr int kChunksPerRow = kRowOut / 16;
+    for (int x = threadIdx.x; x < rows_here * kChunksPerRow; x += 256) {
+      const int r = x / kChunksPerRow, c = x - r * kChunksPerRow;
+      u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16));
+      if (!OUT_F32 && ((r >> 4) & 1)) v = u32x4{v[2], v[3], v[0], v[1]};
+      *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = v;
+    }
+    if (half + 1 < 128 / kStageRows) barrier();
   }
 }
 
@@ -486,10 +756,14 @@ static hipError_t launch_decode_t(const DecodeParams& prm, int grid, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& prm, int grid, bool split, bool out_f32,
+hipError_t launch_decode(const DecodeParams& prm, int max_units, bool split, bool out_f32,
                          hipStream_t st) {
-  constexpr int NB = 6;
-  if (split) return launch_decode_t<NB, true, true>(prm, grid, st);
+  constexpr int NB = 8;
+  const int grid = ((max_units + 7) / 8) * 8;  // whole XCD rounds; extra workgroups exit
+  if (split) {
+    if (out_f32) return launch_decode_t<NB, true, true>(prm, grid, st);
+    return launch_decode_t<NB, true, false>(prm, grid, st);
+  }
   if (out_f32) return launch_decode_t<NB, false, true>(prm, grid, st);
   return launch_decode_t<NB, false, false>(prm, grid, st);
 }

@@ -18,8 +18,9 @@ struct DecodeParams {
   int32_t* split_indptr;       // uniform split: written by the decode kernel
   int B, T, H, page_size, max_blocks;
   int n_rg;                    // workgroups per work item (ceil(T*H/128))
+  int n_units;                 // work items x n_rg (unused with the automatic work list)
   float scale_log2;            // softmax_scale * log2(e)
-  float* part_out;             // split mode: [*,T,H,512] f32
+  void* part_out;              // split mode: [*,T,H,512] f32 or bf16
   float* part_lse;             // split mode: [*,T,H] f32
   void* out;                   // unsplit: [B,T,H,512] bf16 or f32
   float* lse;                  // unsplit: [B,T,H] f32, nullable
@@ -35,7 +36,7 @@ struct PlanParams {
 };
 
 struct MergeParams {
-  const float* part_out;
+  const void* part_out;        // [*,TH,512] f32 or bf16
   const float* part_lse;
   const int32_t* split_indptr;
   int B, TH;
@@ -57,9 +58,10 @@ struct UnabsorbParams {
   int M, H;
 };
 
-hipError_t launch_decode(const DecodeParams& p, int grid, bool split, bool out_f32, hipStream_t st);
+// max_units: upper bound of work items x n_rg (the grid is derived from it)
+hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st);
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
-hipError_t launch_merge(const MergeParams& p, bool out_f32, hipStream_t st);
+hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipStream_t st);
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);
 hipError_t launch_unabsorb(const UnabsorbParams& p, bool latent_f32, hipStream_t st);
 

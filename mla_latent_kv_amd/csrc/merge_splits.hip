@@ -8,87 +8,109 @@
 // merge of (m_r, l_r, o_r); mlxcel Stage 2 merge contract with normalised
 // partials).  Chunks with lse = -inf (no visible key) carry no weight.
 //
-// One workgroup per query row: wave w folds the partials k0 + w, k0 + w + 4, ...
-// into its own running (max, weight sum, 512-wide sum) -- 8 columns per lane --
-// and the four wave states are combined through LDS.  HBM-bound: every partial
-// byte is read once.
+// One wave per query row, 8 of the 512 columns per lane; the row's lse values
+// are wave-uniform scalar loads.  Partials are fp32 or bf16, accumulation is
+// fp32.  HBM-bound: every partial byte is read once, four partials in flight.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mla {
 
-template <bool F32>
+template <bool PART_F32>
+__device__ __forceinline__ void load8(const void* base, size_t elem, f32x4& lo, f32x4& hi) {
+  if constexpr (PART_F32) {
+    const float* src = (const float*)base + elem;
+    lo = *(const f32x4*)src;
+    hi = *(const f32x4*)(src + 4);
+  } else {
+    const u32x4 u = *(const u32x4*)((const uint16_t*)base + elem);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo[2 * i] = __builtin_bit_cast(float, u[i] << 16);
+      lo[2 * i + 1] = __builtin_bit_cast(float, u[i] & 0xFFFF0000u);
+      hi[2 * i] = __builtin_bit_cast(float, u[2 + i] << 16);
+      hi[2 * i + 1] = __builtin_bit_cast(float, u[2 + i] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <bool PART_F32, bool OUT_F32>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-  __shared__ float m_s[4], w_s[4];
-  __shared__ __attribute__((aligned(16))) float o_s[4][kR];
   const int w = wave_id(), l = lane_id();
-  const long long row = blockIdx.x;  // (b, gr)
-  const int b = (int)(row / p.TH);
-  const int gr = (int)(row - (long long)b * p.TH);
+  const long long row = (long long)blockIdx.x * 4 + w;  // (b, gr)
   const int TH = p.TH;
+  if (row >= (long long)p.B * TH) return;
+  const int b = (int)(row / TH);
+  const int gr = (int)(row - (long long)b * TH);
   const int k0 = p.split_indptr[b], k1 = p.split_indptr[b + 1];
   constexpr float kLog2e = 1.4426950408889634f;
+  const float* lse_col = p.part_lse + gr;
 
   float M = -INFINITY;
-  for (int k = k0 + w; k < k1; k += 4) M = fmaxf(M, p.part_lse[(size_t)k * TH + gr]);
+  for (int k = k0; k < k1; ++k) M = fmaxf(M, lse_col[(size_t)k * TH]);
   float wsum = 0.f;
   f32x4 a0 = {}, a1 = {};
   if (M != -INFINITY) {
-#pragma unroll 4
-    for (int k = k0 + w; k < k1; k += 4) {
-      const float x = p.part_lse[(size_t)k * TH + gr];
+    int k = k0;
+    for (; k + 4 <= k1; k += 4) {
+      f32x4 v[4][2];
+      float wk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        load8<PART_F32>(p.part_out, ((size_t)(k + u) * TH + gr) * kR + 8 * l, v[u][0], v[u][1]);
+        const float x = lse_col[(size_t)(k + u) * TH];
+        wk[u] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wsum += wk[u];
+        a0 += wk[u] * v[u][0];
+        a1 += wk[u] * v[u][1];
+      }
+    }
+    for (; k < k1; ++k) {
+      f32x4 v0, v1;
+      load8<PART_F32>(p.part_out, ((size_t)k * TH + gr) * kR + 8 * l, v0, v1);
+      const float x = lse_col[(size_t)k * TH];
       const float wk = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
-      const float* src = p.part_out + ((size_t)k * TH + gr) * kR + 8 * l;
-      const f32x4 v0 = *(const f32x4*)src;
-      const f32x4 v1 = *(const f32x4*)(src + 4);
       wsum += wk;
       a0 += wk * v0;
       a1 += wk * v1;
     }
   }
-  if (l == 0) {
-    m_s[w] = M;
-    w_s[w] = wsum;
-  }
-  *(f32x4*)&o_s[w][8 * l] = a0;
-  *(f32x4*)&o_s[w][8 * l + 4] = a1;
-  __syncthreads();
-  // combine the four wave states; every thread finishes 2 of the 512 columns
-  float Mg = fmaxf(fmaxf(m_s[0], m_s[1]), fmaxf(m_s[2], m_s[3]));
-  float sc[4], tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = (m_s[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_s[i] - Mg) * kLog2e);
-    tot += sc[i] * w_s[i];
-  }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  const int c = 2 * threadIdx.x;
-  float o[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-    o[e] = (sc[0] * o_s[0][c + e] + sc[1] * o_s[1][c + e] + sc[2] * o_s[2][c + e] +
-            sc[3] * o_s[3][c + e]) * inv;
-  const size_t orow = (size_t)b * TH + gr;
-  if constexpr (F32) {
-    float* dst = (float*)p.out + orow * kR + c;
-    dst[0] = o[0];
-    dst[1] = o[1];
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  a0 *= inv;
+  a1 *= inv;
+  const size_t orow = (size_t)row;
+  if constexpr (OUT_F32) {
+    float* dst = (float*)p.out + orow * kR + 8 * l;
+    *(f32x4*)dst = a0;
+    *(f32x4*)(dst + 4) = a1;
   } else {
-    *(uint32_t*)((uint16_t*)p.out + orow * kR + c) = pack_bf16x2(o[0], o[1]);
+    const u32x2 lo = cvt_bf16x4(a0), hi = cvt_bf16x4(a1);
+    *(u32x4*)((uint16_t*)p.out + orow * kR + 8 * l) = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
-  if (threadIdx.x == 0 && p.lse) {
-    p.lse[orow] = tot > 0.f ? Mg + __builtin_amdgcn_logf(tot) * 0.69314718055994530942f
-                            : -INFINITY;
+  if (l == 0 && p.lse) {
+    p.lse[orow] = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * 0.69314718055994530942f : -INFINITY;
   }
 }
 
-hipError_t launch_merge(const MergeParams& prm, bool out_f32, hipStream_t st) {
+template <bool PF, bool OF>
+static void launch_merge_t(const MergeParams& prm, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((merge_kernel<PF, OF>), dim3(grid), dim3(256), 0, st, prm);
+}
+
+hipError_t launch_merge(const MergeParams& prm, bool part_f32, bool out_f32, hipStream_t st) {
   const long long rows = (long long)prm.B * prm.TH;
   if (rows == 0) return hipSuccess;
-  if (out_f32)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)rows), dim3(256), 0, st, prm);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)rows), dim3(256), 0, st, prm);
+  const unsigned grid = (unsigned)((rows + 3) / 4);
+  if (part_f32) {
+    if (out_f32) launch_merge_t<true, true>(prm, grid, st);
+    else launch_merge_t<true, false>(prm, grid, st);
+  } else {
+    if (out_f32) launch_merge_t<false, true>(prm, grid, st);
+    else launch_merge_t<false, false>(prm, grid, st);
+  }
   return hipGetLastError();
 }
 

@@ -71,13 +71,13 @@ def test_unabsorb_validation(lib):
 
 def _decode(lib, **kw):
     a = dict(q_lat=P16, q_pe=P16, kv=P16, nb=64, P=64, bt=P16, mb=64, sl=P16, B=2, T=1, H=128,
-             r=512, dr=64, maxL=4096, scale=0.07, S=1, ws=None, wsb=0, po=None, pl=None, si=None,
-             out=P16, odt=0, lse=None)
+             r=512, dr=64, maxL=4096, scale=0.07, S=1, ws=None, wsb=0, po=None, pdt=1, pl=None,
+             si=None, out=P16, odt=0, lse=None)
     a.update(kw)
     return lib.mla_decode_latent(a["q_lat"], a["q_pe"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"],
                                  a["sl"], a["B"], a["T"], a["H"], a["r"], a["dr"], a["maxL"],
                                  ctypes.c_float(a["scale"]), a["S"], a["ws"], a["wsb"], a["po"],
-                                 a["pl"], a["si"], a["out"], a["odt"], a["lse"], None)
+                                 a["pdt"], a["pl"], a["si"], a["out"], a["odt"], a["lse"], None)
 
 
 def test_decode_validation(lib):
@@ -87,6 +87,7 @@ def test_decode_validation(lib):
     assert _decode(lib, P=2048) == UNSUP
     assert _decode(lib, T=9) == UNSUP
     assert _decode(lib, odt=5) == UNSUP
+    assert _decode(lib, pdt=3) == UNSUP
     assert _decode(lib, scale=0.0) == SHAPE
     assert _decode(lib, scale=float("nan")) == SHAPE
     assert _decode(lib, maxL=0, T=1) == SHAPE    # max_seqlen < T
@@ -104,6 +105,7 @@ def test_decode_validation(lib):
     assert ms.value == 8 and need.value == 0       # uniform splits keep no work list
     assert _decode(lib, S=4, po=P16, pl=P16, si=None) == WS
     assert _decode(lib, S=4, po=P17, pl=P16, si=P16) == ALIGN
+    assert _decode(lib, S=4, po=P17, pdt=0, pl=P16, si=P16) == ALIGN
     assert _decode(lib, B=0, q_lat=None, out=None) == OK
 
 
@@ -123,11 +125,12 @@ def test_workspace_size(lib):
 
 def test_merge_validation(lib):
     f = lib.mla_merge_splits
-    assert f(P16, P16, P16, 2, 1, 128, 256, P16, 0, None, None) == UNSUP
-    assert f(None, P16, P16, 2, 1, 128, 512, P16, 0, None, None) == NULL
-    assert f(P16, P16, P16, 2, 1, 128, 512, P17, 0, None, None) == ALIGN
-    assert f(P16, P16, P16, 2, 1, 128, 512, P16, 9, None, None) == UNSUP
-    assert f(None, None, None, 0, 1, 128, 512, None, 0, None, None) == OK
+    assert f(P16, 1, P16, P16, 2, 1, 128, 256, P16, 0, None, None) == UNSUP
+    assert f(None, 1, P16, P16, 2, 1, 128, 512, P16, 0, None, None) == NULL
+    assert f(P16, 1, P16, P16, 2, 1, 128, 512, P17, 0, None, None) == ALIGN
+    assert f(P16, 1, P16, P16, 2, 1, 128, 512, P16, 9, None, None) == UNSUP
+    assert f(P16, 2, P16, P16, 2, 1, 128, 512, P16, 0, None, None) == UNSUP   # bad partial dtype
+    assert f(None, 0, None, None, 0, 1, 128, 512, None, 0, None, None) == OK
 
 
 def test_binding_names_match_abi():

@@ -26,11 +26,20 @@ def mk():
     return mk
 
 
-def _run_chain(mk, case, d, S):
+def _buffers(mk, case, S, part):
+    import torch
+    if S == 1:
+        return None
+    return mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, "cuda:0",
+                            part_dtype=torch.bfloat16 if part == "bf16" else torch.float32)
+
+
+def _run_chain(mk, case, d, S, part):
     import torch
     q_lat = mk.mla_absorb_q(d["q_nope"], d["w_uk"])
     lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
-                                    case.max_seqlen, SCALE, num_splits=S, out_dtype=torch.bfloat16)
+                                    case.max_seqlen, SCALE, num_splits=S, out_dtype=torch.bfloat16,
+                                    buffers=_buffers(mk, case, S, part))
     out = mk.mla_unabsorb_out(lat, d["w_uv"])
     torch.cuda.synchronize()
     return q_lat, out, lse
@@ -42,20 +51,21 @@ def _check_pairs(got, ref, pairs, what):
     assert_close(g, r, what)
 
 
-@pytest.mark.parametrize("name,S,n_normal,n_mirror", [
-    ("v2lite_tiny", 1, 16, 16),
-    ("v3_b64_l4096", 4, 10, 96),
-    ("v3_b64_l4096", 1, 6, 32),
-    ("v3_ragged_b128", 0, 6, 96),
-    ("v3_long_b4_l131072", 64, 3, 24),
-    ("v3_mtp_b32_t4_h32", 1, 8, 64),
+@pytest.mark.parametrize("name,S,part,n_normal,n_mirror", [
+    ("v2lite_tiny", 1, "-", 16, 16),
+    ("v3_b64_l4096", 4, "bf16", 10, 96),
+    ("v3_b64_l4096", 4, "f32", 4, 32),
+    ("v3_b64_l4096", 1, "-", 6, 32),
+    ("v3_ragged_b128", 0, "bf16", 6, 96),
+    ("v3_long_b4_l131072", 64, "f32", 3, 24),
+    ("v3_mtp_b32_t4_h32", 1, "-", 8, 64),
 ])
-def test_full_size(mk, name, S, n_normal, n_mirror):
-    log(f"[full] {name} num_splits={S}: generating inputs")
+def test_full_size(mk, name, S, part, n_normal, n_mirror):
+    log(f"[full] {name} num_splits={S} partials={part}: generating inputs")
     case = synth.make_case(W[name])
     d = upload(case)
     log(f"[full] {name}: running the GPU chain")
-    q_lat, out, lse = _run_chain(mk, case, d, S)
+    q_lat, out, lse = _run_chain(mk, case, d, S, part)
     out_h = to_f64(out)
     lse_h = to_f64(lse)
     assert np.isfinite(out_h).all() and np.isfinite(lse_h).all(), "non-finite output (stray read?)"
@@ -71,7 +81,8 @@ def test_full_size(mk, name, S, n_normal, n_mirror):
     ql_bits = synth.normal_bf16(case.q_nope.shape[:3] + (512,), 9100, std=0.5)
     lat, lse2 = mk.mla_decode_latent(bf16_tensor(ql_bits, "cuda:0"), d["q_pe"], d["kv_cache"],
                                      d["block_table"], d["seqlens"], case.max_seqlen, SCALE,
-                                     num_splits=S, out_dtype=torch.float32)
+                                     num_splits=S, out_dtype=torch.float32,
+                                     buffers=_buffers(mk, case, S, part))
     torch.cuda.synchronize()
     mpairs = sample_pairs(case.B, case.H, n_mirror, seed=37)
     log(f"[full] {name}: absorbed mirror on {len(mpairs)} pairs")

@@ -43,6 +43,10 @@ def small_cases():
                                    seed=2106),
         "page256_h16": synth.scaled(W["v3_b64_l4096"], B=2, H=16, page_size=256,
                                     lengths=(600, 257), seed=2107),
+        # page 16, T=4: with 2 or 3 splits the last chunk of the 35-token sequence
+        # starts at 32 = L - T + 1, where query t=0 sees none of its keys
+        "mtp_p16_tail": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, page_size=16, lengths=(35, 51),
+                                     seed=2108),
     }
 
 
@@ -120,16 +124,18 @@ def test_end_to_end_vs_normal_path(mk, name):
     assert_close(to_f64(lse), ref_lse, "lse")
 
 
+@pytest.mark.parametrize("part", ["f32", "bf16"])
 @pytest.mark.parametrize("S", [2, 3, 7])
-@pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64"])
-def test_split_partials_and_merge(mk, name, S):
+@pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64", "mtp_p16_tail"])
+def test_split_partials_and_merge(mk, name, S, part):
     import torch
-    log(f"[split] {name} S={S}")
+    log(f"[split] {name} S={S} partials={part}")
     case = _case(name)
     d = upload(case)
     ql_bits = _stage_q_lat(case, 7100 + S)
     q_lat = bf16_tensor(ql_bits, "cuda:0")
-    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, "cuda:0")
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, "cuda:0",
+                           part_dtype=torch.float32 if part == "f32" else torch.bfloat16)
     lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
                                     case.max_seqlen, SCALE, num_splits=S, out_dtype=torch.float32,
                                     buffers=buf)
@@ -144,7 +150,7 @@ def test_split_partials_and_merge(mk, name, S):
     empty = np.isneginf(ref_pl)
     assert np.array_equal(np.isneginf(got_pl), empty), "empty partials must carry lse = -inf"
     assert_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
-    assert_close(buf.part_out[:n].cpu().numpy(), ref_po, "partial out")
+    assert_close(to_f64(buf.part_out[:n]), ref_po, "partial out")
     ref_lat, ref_lse = oracle.latent_attention(case, q64)
     assert_close(to_f64(lat), ref_lat, "merged latent")
     assert_close(to_f64(lse), ref_lse, "merged lse")
@@ -165,22 +171,68 @@ def test_auto_split(mk):
     assert_close(to_f64(lse), ref_lse, "lse")
 
 
-def test_merge_of_oracle_partials(mk):
-    """The merge kernel alone, fed partials the oracle computed (as f32)."""
+@pytest.mark.parametrize("part", ["f32", "bf16"])
+def test_merge_of_oracle_partials(mk, part):
+    """The merge kernel alone, fed partials the oracle computed (rounded to the
+    partial dtype on the host; the expected value merges the same rounded values)."""
     import torch
-    log("[merge] oracle partials")
+    log(f"[merge] oracle partials ({part})")
     case = _case("mtp_t4_h32")
     q64 = bits_to_f64(_stage_q_lat(case, 7300))
     plan = oracle.split_plan(case.seqlens, 5, case.page_size)
     po, pl = oracle.latent_attention(case, q64, plan=plan)
-    ref, ref_lse = oracle.merge(po, pl, plan[0])
     dev = "cuda:0"
-    out, lse = mk.mla_merge_splits(torch.from_numpy(po.astype(np.float32)).to(dev),
-                                   torch.from_numpy(pl.astype(np.float32)).to(dev),
+    if part == "f32":
+        po_in = po.astype(np.float32)
+        t_po = torch.from_numpy(po_in).to(dev)
+    else:
+        bits = synth.f32_to_bf16_bits(po.astype(np.float32))
+        po_in = bits_to_f64(bits)
+        t_po = bf16_tensor(bits, dev)
+    pl_in = pl.astype(np.float32)
+    ref, ref_lse = oracle.merge(po_in.astype(np.float64), pl_in.astype(np.float64), plan[0])
+    out, lse = mk.mla_merge_splits(t_po, torch.from_numpy(pl_in).to(dev),
                                    torch.from_numpy(plan[0]).to(dev), case.B,
                                    out_dtype=torch.float32)
     assert_close(to_f64(out), ref, "merged")
     assert_close(to_f64(lse), ref_lse, "merged lse")
+
+
+def _hot_key_case(name, seed, hot_token, gain=16):
+    """A case whose sequence 0 holds, at logical token `hot_token`, a key row
+    c = gain * q~[0,0,0,:]: head 0's score there exceeds every earlier score by
+    about gain * |q~|^2 * scale (about 200 in log2 units for gain 16), far past
+    the first tile's reference.  Returns (case, absorbed-query bits)."""
+    case = _case(name)
+    ql_bits = _stage_q_lat(case, seed)
+    P = case.page_size
+    blk, off = int(case.block_table[0, hot_token // P]), hot_token % P
+    q0 = bits_to_f64(ql_bits[0, 0, 0, :])
+    case.kv_cache[blk, off, :512] = synth.f32_to_bf16_bits((gain * q0).astype(np.float32))
+    return case, ql_bits
+
+
+@pytest.mark.parametrize("S", [1, 2, 0])
+@pytest.mark.parametrize("hot_token", [3, 137, 290])
+def test_score_growth_past_reference(mk, S, hot_token):
+    """A score far above the first tile's maximum (a replay of the work unit
+    with a raised reference) gives the same result as ordinary inputs: exact
+    softmax, no overflow leaking from the discarded pass."""
+    import torch
+    log(f"[growth] hot key at {hot_token}, num_splits={S}")
+    case, ql_bits = _hot_key_case("v3_b3_l300", 7500 + hot_token, hot_token)
+    d = upload(case)
+    lat, lse = mk.mla_decode_latent(bf16_tensor(ql_bits, "cuda:0"), d["q_pe"], d["kv_cache"],
+                                    d["block_table"], d["seqlens"], case.max_seqlen, SCALE,
+                                    num_splits=S, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_lat, ref_lse = oracle.latent_attention(case, bits_to_f64(ql_bits))
+    # head 0 of sequence 0 attends almost only to the hot row (whose c is 16 q~)
+    hot = bits_to_f64(case.kv_cache[int(case.block_table[0, hot_token // case.page_size]),
+                                    hot_token % case.page_size, :512])
+    assert float(np.max(np.abs(ref_lat[0, 0, 0] - hot))) < 1e-9 * float(np.max(np.abs(hot)))
+    assert_close(to_f64(lat), ref_lat, "latent")
+    assert_close(to_f64(lse), ref_lse, "lse")
 
 
 def test_page_placement_is_bitwise_invisible(mk):
