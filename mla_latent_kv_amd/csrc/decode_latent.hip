@@ -64,6 +64,10 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Wait until at most `tiles` of this wave's most recent tile loads are in
 // flight (PER = load instructions per tile issued by this wave).
@@ -473,33 +477,48 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     // Two-stage pipeline.  Step i (after its barrier): value MFMAs of tile i
     // (probabilities P(i) written during step i-1), score MFMAs of tile i+2,
     // and the softmax of tile i+1 (scores from step i-1) producing P(i+1).
-    // Resident ring buffers: tiles i, i+1, i+2; up to NB-4 more in flight.
+    // The first K operands of tile i+3 are read at the end of step i, so every
+    // step starts with MFMAs; tile i+3 has therefore landed before barrier i.
+    // Resident ring buffers: tiles i .. i+3; up to NB-5 more in flight.
+    constexpr int PF = 4;  // K operand reads in flight
+    bf16x8 kb[PF];
+    auto k_first = [&](int it) {
+      const uint32_t kbase = tiles_lds + (it % NB) * kTileBytes + k_lane;
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
+    };
     f32x4 s0 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, s1 = s0;  // scores of tile i+1
     if (ntiles > 0) {
-      // prologue: tiles 0 and 1 landed; P(0) and the scores of tile 1
-      const int ahead = max(0, min(NB - 1, ntiles) - 2);
-      if (w < 2) wait_tiles<5, NB - 3>(ahead);
-      else wait_tiles<4, NB - 3>(ahead);
+      // prologue: tiles 0, 1 and 2 landed; P(0), the scores of tile 1 and the
+      // first K operands of tile 2
+      const int ahead = max(0, min(NB - 1, ntiles) - 3);
+      if (w < 2) wait_tiles<5, NB - 4>(ahead);
+      else wait_tiles<4, NB - 4>(ahead);
       barrier();
       clear_tail(0);
       if (ntiles > 1) clear_tail(1);
+      if (ntiles > 2) clear_tail(2);
       f32x4 t0, t1;
       scores_plain(0, t0, t1);
       softmax_tile(t0, t1, 0);
       if (ntiles > 1) scores_plain(1, s0, s1);
+      k_first(2);
     }
     for (int i = 0; i < ntiles; ++i) {
       const bool do_qk = i + 2 < ntiles;
       const bool do_sm = i + 1 < ntiles;
       const bool do_issue = i + NB - 1 < ntiles;
-      // tile i+2 must have landed; up to NB-4 later tiles may stay in flight
-      if (do_qk) {
-        if (w < 2) wait_tiles<5, NB - 4>(min(NB - 4, ntiles - i - 3));
-        else wait_tiles<4, NB - 4>(min(NB - 4, ntiles - i - 3));
+      // tile i+3 must have landed; up to NB-5 later tiles may stay in flight
+      if (i + 3 < ntiles) {
+        if (w < 2) wait_tiles<5, NB - 5>(min(NB - 5, ntiles - i - 4));
+        else wait_tiles<4, NB - 5>(min(NB - 5, ntiles - i - 4));
       }
-      wait_lgkm0();  // this wave's probability writes and tail clears
+      // this wave's probability writes and tail clears must be complete; LDS
+      // operations complete in order, so allowing only the PF K reads issued
+      // last (by k_first) to remain in flight is enough
+      wait_lgkm<PF>();
       barrier();
-      if (do_qk) clear_tail(i + 2);
+      if (i + 3 < ntiles) clear_tail(i + 3);
       if (do_issue) issue_prep(i + NB - 1);
 
       // softmax of tile i+1 done up front when some row still needs its
@@ -524,10 +543,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       vop[0] = join8(lds_tr16(vb0), lds_tr16(vb1));
       // (the score MFMAs also run in the last two steps, on a stale buffer; their
       // results are discarded)
-      constexpr int PF = 4;
-      bf16x8 kb[PF];
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
       f32x4 n0 = {}, n1 = {};  // scores of tile i+2
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
@@ -537,13 +552,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], n0, 0, 0, 0);
           n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], n1, 0, 0, 0);
         }
-        if (ks >= 1 && ks <= 16) {
-          const int v = ks - 1, f = v >> 2, rb = v & 3;
+        // value MFMAs: none in steps 0-3 (their operands, read after the
+        // barrier, are still arriving), one per step in 4-13, two in 14-16
+        constexpr int kPvBegin[18] = {0, 0, 0, 0, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16};
+        constexpr int kPvEnd[18] = {0, 0, 0, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16, 16};
+#pragma unroll
+        for (int v = kPvBegin[ks]; v < kPvEnd[ks]; ++v) {
+          const int f = v >> 2, rb = v & 3;
           mfma_pv(acc[f][rb], vop[f & 1], pb[rb]);
         }
-        // V operand of column block f+1 read a block ahead (two alternating slots)
-        if (ks == 1 || ks == 5 || ks == 9) {
-          const int f = (ks >> 2) + 1;
+        // V operand of column block f read a block ahead (two alternating slots)
+        if (ks == 2 || ks == 8 || ks == 12) {
+          const int f = ks == 2 ? 1 : ks == 8 ? 2 : 3;
           vop[f & 1] = join8(lds_tr16(vb0 + 1024 * f), lds_tr16(vb1 + 1024 * f));
         }
         {
@@ -577,6 +597,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if (grow) sm_grow();
+      k_first(i + 3);  // (a stale buffer near the end; never used then)
       const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       s0 = do_qk ? n0 : ninf;
       s1 = do_qk ? n1 : ninf;
