@@ -8,49 +8,44 @@
 // where row j of the cache is [c_j (512) || kpe_j (64)], found through the
 // block table (M5.8 0x05).  All heads share the one latent KV head, so every
 // 1152-byte row is read from HBM once per workgroup and reused by all 128
-// query rows: the score GEMM is [128 x 576] x [576 x tile] and the value GEMM
-// is [128 x tile] x [tile x 512], both on the matrix cores in bf16 with fp32
+// query rows; both GEMMs run on the matrix cores in bf16 with fp32
 // accumulation.  The softmax is accumulated over KV tiles against one
 // reference maximum per row and normalised once at the end (M5.8 0x0A: tiles
 // are never normalised independently).
 //
-// Workgroup layout (256 threads = 4 waves of 64, one workgroup per CU):
-//  * KV tiles of 16 tokens (18 KB) stream HBM -> LDS with direct-to-LDS loads
-//    into a ring of NB buffers.  Every wave issues a quarter of each tile's 18
-//    load instructions.
-//  * Score phase: wave w owns query rows [32w, 32w+32) and computes
-//    S^T[16 tok x 32 rows] with 16x16x32 MFMAs; the K operand is read from LDS
-//    with ds_read_b128, the query lives in registers for the whole kernel.
+// Workgroup layout (256 threads = 4 waves of 64, one workgroup per CU).  Wave w
+// owns query rows [32w, 32w + 32) for the whole computation:
+//  * KV rows stream HBM -> LDS with direct-to-LDS loads in steps of 32 tokens
+//    (two 16-row halves, 36 KB) into a ring of NB step buffers; waves 0-1 load
+//    the first half of every step, waves 2-3 the second.
+//  * Scores: S^T[32 tok x 32 rows] = K[32 x 576] q~^T with 36 32x32x16 MFMAs;
+//    K comes from LDS (ds_read_b128), the query rows live in registers.  A lane
+//    then holds 16 scores of one query row.
 //  * Softmax: log2 domain against a per-row reference m_ref (the max of the
-//    row's first tile with a visible key), so exponentials are bounded by
+//    row's first step with a visible key), so exponentials are bounded by
 //    2^kLazy and the fp32 accumulator is never rescaled.  Each lane checks its
-//    own scores against m_ref + kLazy; only when one exceeds it is the row max
-//    reduced across lanes, m_ref raised and the work unit replayed from its
-//    first tile (exact for any finite scores; never taken for scores of
-//    ordinary magnitude).
-//  * Probabilities (bf16) of all 128 rows are exchanged through LDS (two
-//    buffers, alternating tiles).
-//  * Value phase: wave w owns latent columns [128w, 128w+128) of all 128 rows
-//    (O^T accumulator 128 x 128 fp32 = 256 registers) and multiplies
-//    V^T[32 cols x 16 tok] (transposing LDS reads) by P^T[16 tok x 32 rows]
-//    with 32x32x16 MFMAs.  Splitting the value GEMM by columns rather than by
-//    rows means each V element is read from LDS once per workgroup instead of
-//    once per wave.
-//  * Software pipeline, one barrier per tile: after the barrier of step i the
-//    wave computes the scores of tile i+1, then issues the value MFMAs of tile
-//    i with the softmax of tile i+1 placed between them, so the vector ALU
-//    work runs while the matrix core is busy.
+//    own scores against m_ref + kLazy; only when one exceeds it is m_ref
+//    raised and the work unit replayed from its first step (exact for any
+//    finite scores; never taken for scores of ordinary magnitude).
+//  * Values: O^T[512 cols x 32 rows] += V^T P^T with 32 32x32x16 MFMAs per step
+//    (256 accumulator registers).  The score accumulator layout is exactly the
+//    P^T operand layout (with the token order inside each 16-token block taken
+//    as the MFMA's k order and V read in the same order), so the
+//    probabilities never leave the registers; V comes from LDS through
+//    transposing reads (ds_read_b64_tr_b16).
+//  * Software pipeline, one barrier per 32-token step: the value MFMAs of step
+//    i and the score MFMAs of step i+1 form one MFMA stream; the softmax of
+//    step i+1 runs on the vector ALU under the last value MFMAs; LDS operand
+//    reads and this wave's load instructions for step i+NB-1 sit in between.
+//    A single wave per SIMD issues at most one instruction every four cycles,
+//    so the design keeps non-MFMA instructions few: about 330 per 32 tokens
+//    for 68 MFMAs (2176 matrix-core cycles).
 //
-// Tile LDS layout (chunk-major): the 16-byte chunk c (c < 72) of tile row t is
-// stored at chunk position 16c + (t ^ g(c & 3)) with g = (0, 12, 8, 4).  A K
-// read (16 rows of 4 chunks) and a transposing V read are then both free of
-// bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT; g = (0, 4, 8,
-// 12), the obvious choice, makes the 16-byte K reads conflict 2-way); the
+// LDS layout of a 16-row half (chunk-major): the 16-byte chunk c (c < 72) of
+// row t is stored at chunk position 16c + (t ^ g(c & 3)), g = (0, 12, 8, 4).
+// The K reads (32 rows x 2 chunks) and the transposing V reads are then both
+// free of bank conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT); the
 // direct-to-LDS loads write 1 KB contiguous.
-//
-// Probability buffer: row R (of 128) holds 16 bf16 = two 16-byte chunks, chunk c
-// (tokens 8c..8c+7) at byte 32R + 16(c ^ s(R)), s(R) = ((R >> 2) ^ (R >> 4)) & 1;
-// 16-byte writes and reads of it are conflict-free.
 #include <type_traits>
 
 #include "common.hpp"
@@ -58,7 +53,11 @@
 
 namespace mla {
 
-constexpr float kLazy = 64.0f;  // log2-domain growth of the max tolerated before a replay
+constexpr float kLazy = 64.0f;               // log2-domain growth of the max tolerated before a replay
+constexpr int kStepTok = 32;                 // tokens per pipeline step
+constexpr int kStepBytes = 2 * kTileBytes;   // two 16-row halves
+constexpr int kQk = kRow / 16;               // 36 score MFMAs per step (k = 16 each)
+constexpr int kPv = 2 * (kR / 32);           // 32 value MFMAs per step (2 token blocks x 16 column blocks)
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -69,50 +68,31 @@ __device__ __forceinline__ void wait_lgkm() {
   asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most `tiles` of this wave's most recent tile loads are in
-// flight (PER = load instructions per tile issued by this wave).
-template <int PER, int MAXT>
-__device__ __forceinline__ void wait_tiles(int tiles) {
-  static_assert(MAXT <= 6, "extend the switch");
-  switch (tiles < MAXT ? tiles : MAXT) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<PER>(); break;
-    case 2: wait_vm<2 * PER>(); break;
-    case 3: if constexpr (MAXT >= 3) wait_vm<3 * PER>(); break;
-    case 4: if constexpr (MAXT >= 4) wait_vm<4 * PER>(); break;
-    case 5: if constexpr (MAXT >= 5) wait_vm<5 * PER>(); break;
-    default: if constexpr (MAXT >= 6) wait_vm<6 * PER>(); break;
+// Hide a value's known bits from the compiler, so that address arithmetic on it
+// stays base + constant (folded into the LDS instruction's offset field).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Compile-time loop: f(integral_constant<int, S>) for S = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
-// Cross-lane pair exchange.  v_permlane16_swap exchanges the odd 16-lane rows of
-// its first operand with the even rows of its second; with both operands
-// holding v, lane l ends up with v of lanes l and l^16 (permlane32: l and l^32).
-// Written as inline assembly: the builtin has been seen to compile to code that
-// reads only one of the two results.  The swap reads its operands two wait
-// states after a VALU write at the earliest, hence the s_nop.
-__device__ __forceinline__ void xpair16(float v, float& a, float& b) {
-  a = v;
-  b = v;
-  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
+// v of lane l and of lane l ^ 32.  v_permlane32_swap exchanges the upper half
+// of its first operand with the lower half of its second; it reads its
+// operands two wait states after a VALU write at the earliest, hence the s_nop.
+// (Inline assembly: the builtin has been seen to compile to code that reads
+// only one of the two results.)
 __device__ __forceinline__ void xpair32(float v, float& a, float& b) {
   a = v;
   b = v;
   asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-// max / sum over the four lanes l, l^16, l^32, l^48
-__device__ __forceinline__ float max4lanes(float v) {
-  float a, b;
-  xpair16(v, a, b);
-  xpair32(fmaxf(a, b), a, b);
-  return fmaxf(a, b);
-}
-__device__ __forceinline__ float sum4lanes(float v) {
-  float a, b;
-  xpair16(v, a, b);
-  xpair32(a + b, a, b);
-  return a + b;
 }
 
 // max of four floats in two VALU ops (v_max3 does not canonicalise its inputs;
@@ -136,11 +116,12 @@ __device__ __forceinline__ void lds_st64(uint32_t addr, u32x2 v) {
   *(__attribute__((address_space(3))) u32x2*)(uintptr_t)addr = v;
 }
 
-// Value-phase MFMA with its accumulator pinned to AGPRs (the 128x128 fp32 O^T
+// Value-phase MFMA with its accumulator pinned to AGPRs (the 512x32 fp32 O^T
 // block of a wave fills all 256 of them); written as inline assembly so that
-// the score accumulators, which the softmax reads, stay in VGPRs.  The operands
-// come straight from LDS reads (the compiler's wait counts cover them); the
-// accumulator is next touched by VALU code only after mfma_drain().
+// the score accumulator, which the softmax reads, stays in VGPRs.  The operands
+// come straight from LDS reads and register conversions (the compiler's wait
+// counts cover the reads); the accumulator is next touched by VALU code only
+// after mfma_drain().
 __device__ __forceinline__ void mfma_pv(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -149,28 +130,40 @@ __device__ __forceinline__ void mfma_pv(f32x16& acc, const bf16x8& a, const bf16
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Row swizzle of the tile layout and the position (in 16-byte units) of chunk c
-// of tile row t.
+// of half-tile row t.
 __device__ __forceinline__ int tile_swz(int c) { return (-4 * c) & 12; }
 __device__ __forceinline__ int tile_pos(int c, int t) { return 16 * c + (t ^ tile_swz(c & 3)); }
-// probability-buffer chunk swap of row r
-__device__ __forceinline__ int pbuf_swz(int r) { return ((r >> 2) ^ (r >> 4)) & 1; }
-// v_permlane16_swap of two different registers: afterwards a = [a.r0, b.r0,
-// a.r2, b.r2] and b = [a.r1, b.r1, a.r3, b.r3] (r = 16-lane row)
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
-  asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+
+// ---- stream schedule of one step: 68 MFMA slots ----
+// slots 0-7: value MFMAs v = 0..7; slots 8-51: score MFMAs ks = 0..35 with value
+// MFMAs v = 8..15 after every fourth score MFMA; slots 52-67: value MFMAs
+// v = 16..31, under which the softmax of the next step runs.
+struct Slot {
+  int qk;  // score MFMA k-step or -1
+  int pv;  // value MFMA index or -1
+};
+constexpr int kSlots = kQk + kPv;
+constexpr Slot slot_of(int s) {
+  if (s < 8) return Slot{-1, s};
+  if (s < 52) {
+    const int x = s - 8;  // 44 slots: pattern Q Q Q Q P (x8), then Q Q Q Q
+    if (x < 40) return (x % 5 == 4) ? Slot{-1, 8 + x / 5} : Slot{x / 5 * 4 + x % 5, -1};
+    return Slot{32 + (x - 40), -1};
+  }
+  return Slot{-1, 16 + (s - 52)};
 }
+// value MFMA v: token block kb = v >> 4 (16 tokens), column block cb = v & 15
 
 template <int NB, bool SPLIT, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
-  // tile ring; after the last tile it is reused to stage the 128 KB output block
-  constexpr int kRingBytes = NB * kTileBytes > 128 * 1024 ? NB * kTileBytes : 128 * 1024;
+  // step ring; after the last step it is reused to stage the 128 KB output block
+  constexpr int kRingBytes = NB * kStepBytes > 128 * 1024 ? NB * kStepBytes : 128 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kRingBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t pbuf[2 * kRowsPerWG * kTile];
-  __shared__ __attribute__((aligned(16))) float inv_s[kRowsPerWG];
   __shared__ unsigned flag_s;
 
   const int w = wave_id();
   const int l = lane_id();
+  const int hl = l >> 5;  // lane half: token sub-block 4*hl of each 8-token group
 
   // ---- work unit.  Units u = item * n_rg + rg are dealt to the XCDs in
   // contiguous ranges (workgroup i runs on XCD i % 8), so the splits of one
@@ -222,83 +215,108 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   const int P = p.page_size;
   const int row0 = rg * kRowsPerWG;
 
-  // ---- query rows of this wave (score phase) and their visible limits ----
-  // dd[nb] = (first invisible key of the row) - j0 - 4(l>>4): key r of the lane's
-  // 4-key group in tile i is visible iff r < dd[nb] - 16 i.  Padding rows past
+  // ---- this lane's query row (lanes l and l ^ 32 share it) ----
+  // q[ks] holds elements 16ks + 8hl .. +7 of [q~ || q_pe] (the B operand of the
+  // score MFMA).  Key j of the row is visible iff j < lim; padding rows past
   // T*H get a zero query and see every key (their scores are 0, never stored).
-  bf16x8 q[2][18];
-  int dd[2];
+  const int rloc = 32 * w + (l & 31);
+  const int grow_ = row0 + rloc;
+  bf16x8 q[kQk];
+  int lim = j1;
+  if (grow_ < TH) {
+    const int t = grow_ / H;
+    const int h = grow_ - t * H;
+    lim = min(L - T + t + 1, j1);
+    const uint16_t* ql = p.q_lat + ((size_t)(b * T + t) * H + h) * kR + 8 * hl;
+    const uint16_t* qp = p.q_pe + ((size_t)(b * T + t) * H + h) * kDR + 8 * hl;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int gr = row0 + 32 * w + 16 * nb + (l & 15);
-    int lim = j1;
-    if (gr < TH) {
-      const int t = gr / H;
-      const int h = gr - t * H;
-      lim = min(L - T + t + 1, j1);
-      const uint16_t* ql = p.q_lat + ((size_t)(b * T + t) * H + h) * kR + 8 * (l >> 4);
-      const uint16_t* qp = p.q_pe + ((size_t)(b * T + t) * H + h) * kDR + 8 * (l >> 4);
+    for (int ks = 0; ks < kR / 16; ++ks) q[ks] = *(const bf16x8*)(ql + 16 * ks);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) q[nb][ks] = *(const bf16x8*)(ql + 32 * ks);
+    for (int ks = 0; ks < kDR / 16; ++ks) q[kR / 16 + ks] = *(const bf16x8*)(qp + 16 * ks);
+  } else {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) q[nb][16 + ks] = *(const bf16x8*)(qp + 32 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) q[nb][ks] = bf16x8{};
-    }
-    dd[nb] = lim - j0 - 4 * (l >> 4);
+    for (int ks = 0; ks < kQk; ++ks) q[ks] = bf16x8{};
   }
+  // score register r of step it is token j0 + 32 it + tok(r) + 4 hl with
+  // tok(r) = 8 (r >> 2) + (r & 3): visible iff tok(r) < dd - 32 it
+  const int dd = lim - j0 - 4 * hl;
 
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+  const int nsteps = (j1 - j0 + kStepTok - 1) / kStepTok;
   const uint32_t tiles_lds = lds_addr_of(tiles);
   const uint8_t* cache = (const uint8_t*)p.cache;
   const int32_t* bt_row = p.block_table + (size_t)b * p.max_blocks;
 
-  // physical pages of logical pages [pg_base, pg_base + 64), one per lane
-  int pg_base = j0 / P;
-  int pg_vec = 0;
-  {
-    const int pg = pg_base + l;
-    if (pg < p.max_blocks && pg * P < j1) pg_vec = bt_row[pg];
-  }
+  // ---- loads.  Wave w loads half hw = w >> 1 of every step (16 rows, 18 load
+  // instructions shared by waves 2hw and 2hw+1: instruction kk = (w & 1) + 2n,
+  // n < 9).  Instruction kk fills chunk positions [64kk, 64kk + 64) of the
+  // half: lane l brings chunk 4kk + (l >> 4) of row (l & 15) ^ g(l >> 4).
+  // Physical pages come from a window of 64 block-table entries held one per
+  // lane; the page of the next half-tile is tracked incrementally.
+  const int hw = w >> 1;
+  const uint32_t dma_voff = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4) + 64 * (w & 1);
+  int pg_base = 0, pg_vec = 0;
+  auto load_window = [&](int base) {
+    pg_base = base;
+    const int pg = base + l;
+    pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
+  };
+  int dma_page = 0, dma_off = 0;  // page and in-page row of this wave's next half-tile
+  auto dma_reset = [&]() {
+    const int jt = j0 + 16 * hw;
+    dma_page = jt / P;
+    dma_off = jt - dma_page * P;
+  };
+  dma_reset();
+  load_window(dma_page);
   if (threadIdx.x == 0) flag_s = 0u;
   // q and the first page ids must be complete before any tile load is in flight:
   // this wait is visible to the compiler, so it does not later wait for them
   // against the (compiler-invisible) tile loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Load tile `it` into ring buffer it % NB: this wave issues instructions
-  // k = w, w+4, ... of the tile's 18; instruction k fills chunk positions
-  // [64k, 64k+64), i.e. chunks 4k .. 4k+3 of all 16 rows.  Lane l writes
-  // position 64k + l: chunk 4k + (l>>4) of row (l & 15) ^ g(l>>4).
-  const uint32_t dma_lane = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4);
-  // Tile loads are issued a few instructions at a time between the MFMAs:
-  // issue_prep(it) selects tile `it` (its page and ring buffer), issue_part(n)
-  // issues this wave's n-th load instruction of it (k = w + 4n < 18).  The
-  // tile's global base is wave-uniform (scalar registers); lane offsets are
-  // dma_lane + 64w + 256n.
-  const uint32_t dma_voff = dma_lane + 64 * w;
   const uint8_t* dma_base = cache;
   uint32_t dma_dst = 0;
+  // Loads of steps past the last one (the pipeline issues NB-1 steps ahead
+  // unconditionally) repeat the previous step's rows, which the L2 still holds,
+  // into the ring buffer that no wave reads any more; this keeps the issue
+  // path and the wait counts free of branches.
   auto issue_prep = [&](int it) {
-    const int jt = j0 + it * kTile;
-    const int page = jt / P;
-    if (page >= pg_base + 64) {
-      pg_base += 64;
-      const int pg = pg_base + l;
-      pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
-      // complete the reload here, visibly to the compiler, so that the common
-      // path carries no wait for it (a vector-memory wait would also drain the
-      // in-flight tile loads)
-      __builtin_amdgcn_s_waitcnt(0);
+    if (it < nsteps) {
+      int page = dma_page, off = dma_off;
+      if (j0 + kStepTok * it + 16 * hw >= j1) {
+        // this half lies past the end: load the step's first half again (valid
+        // rows of a valid page); its rows are cleared before any use
+        off -= 16;
+        if (off < 0) {
+          off += P;
+          --page;
+        }
+      }
+      if (page < pg_base || page >= pg_base + 64) {
+        load_window(page);
+        // complete the reload here, visibly to the compiler, so that the common
+        // path carries no wait for it (a vector-memory wait would also drain the
+        // in-flight tile loads)
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      const int phys = __builtin_amdgcn_readlane(pg_vec, page - pg_base);
+      dma_base = cache + ((size_t)phys * P + off) * kRowBytes;
+      // advance to the same half of the next step (page_size is a multiple of 16)
+      dma_off += kStepTok;
+      if (dma_off >= P) {
+        dma_off -= P;
+        ++dma_page;
+        if (dma_off >= P) {
+          dma_off -= P;
+          ++dma_page;
+        }
+      }
     }
-    const int phys = __builtin_amdgcn_readlane(pg_vec, page - pg_base);
-    dma_base = cache + ((size_t)phys * P + (jt - page * P)) * kRowBytes;
-    dma_dst = tiles_lds + (it % NB) * kTileBytes + 1024 * w;
+    dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
   };
   auto issue_part = [&](auto n_const) {
     constexpr int n = decltype(n_const)::value;
-    if (w + 4 * n < 18) dma16s(dma_voff + 256 * n, dma_base, dma_dst + 4096 * n);
+    dma16s(dma_voff + 128 * n, dma_base, dma_dst + 2048 * n);
   };
   auto issue = [&](int it) {
     issue_prep(it);
@@ -307,150 +325,157 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     issue_part(std::integral_constant<int, 2>{});
     issue_part(std::integral_constant<int, 3>{});
     issue_part(std::integral_constant<int, 4>{});
+    issue_part(std::integral_constant<int, 5>{});
+    issue_part(std::integral_constant<int, 6>{});
+    issue_part(std::integral_constant<int, 7>{});
+    issue_part(std::integral_constant<int, 8>{});
   };
-  // Rows past the end of the range were loaded from the rest of the page, which
-  // may hold anything: clear their value chunks so that 0-probability x row is 0.
+  // Rows of the last step past the end of the range hold other tokens (or are
+  // loaded twice): clear their value chunks so that 0-probability x row is 0.
   auto clear_tail = [&](int it) {
-    const int nvalid = j1 - (j0 + it * kTile);
-    if (nvalid >= kTile) return;
-    const uint32_t buf = tiles_lds + (it % NB) * kTileBytes;
-    for (int x = threadIdx.x; x < 64 * kTile; x += 256) {
-      const int c = x >> 4, t = x & 15;
-      if (t >= nvalid)
-        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(buf + tile_pos(c, t) * 16) = u32x4{0u, 0u, 0u, 0u};
+    const int nvalid = j1 - (j0 + kStepTok * it);
+    if (nvalid >= kStepTok) return;
+    const uint32_t buf = tiles_lds + (it % NB) * kStepBytes;
+    for (int x = threadIdx.x; x < 2 * 64 * 16; x += 256) {
+      const int hf = x >> 10, c = (x >> 4) & 63, t = x & 15;
+      if (16 * hf + t >= nvalid)
+        *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(buf + hf * kTileBytes + tile_pos(c, t) * 16) =
+            u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  // score-phase K reads: lane reads chunk 4ks + (l>>4) of tile row (l & 15)
-  const uint32_t k_lane = ((l >> 4) * 16 + ((l & 15) ^ tile_swz(l >> 4))) * 16;
-  // value-phase transposing reads: group g = l>>4, lane j = l&15; read r covers
-  // rows 8(g>>1) + 4r + (j>>2) and columns 32fb + 16(g&1) + 4(j&3) .. +3, i.e.
-  // chunk 4fb + cl with cl = 2(g&1) + ((j>>1)&1), byte 8(j&1) of the chunk
+  // score-phase K reads (A operand): lane reads row l & 31 of the step (half
+  // (l >> 4) & 1), chunk 2ks + hl; address buf + k_lane[ks & 1] + 512 ks
+  uint32_t k_lane[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    k_lane[e] = kTileBytes * ((l >> 4) & 1) + 256 * hl + 16 * ((l & 15) ^ tile_swz(2 * e + hl));
+  // value-phase transposing reads (A operand V^T of column block cb, token block
+  // kb): group g = l >> 4, lane j = l & 15; read r covers tokens
+  // 16kb + 4(g>>1) + 8r + (j>>2) and columns 32cb + 16(g&1) + 4(j&3) .. +3, i.e.
+  // chunk 4cb + cl with cl = 2(g&1) + ((j>>1)&1), byte 8(j&1) of the chunk;
+  // address buf + kb * kTileBytes + 1024 cb + v_lane[r]
   uint32_t v_lane[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int g = l >> 4, j = l & 15;
-    const int tok = 8 * (g >> 1) + 4 * r + (j >> 2);
+    const int tok = 4 * (g >> 1) + 8 * r + (j >> 2);
     const int cl = 2 * (g & 1) + ((j >> 1) & 1);
     v_lane[r] = (16 * cl + (tok ^ tile_swz(cl))) * 16 + 8 * (j & 1);
   }
-  // probability buffer: after the row exchange in sm_store lane l holds tokens
-  // 8(l>>5) .. +7 of row 32w + (l & 31); the value phase reads row 32rb + (l & 31),
-  // chunk l>>5 (the P^T operand layout)
-  const uint32_t pbuf_lds = lds_addr_of(pbuf);
-  const uint32_t p_rd = (l & 31) * 32 + 16 * ((l >> 5) ^ pbuf_swz(l & 31));
-  const uint32_t p_wr = 32 * 32 * w + p_rd;
   const float sl2 = p.scale_log2;
   const float lazy_raw = kLazy / sl2;
 
   // Per-row softmax reference (log2 domain) and the raw-score threshold above
   // which a replay is needed; nmb = -m_ref (0 while the row has no visible key).
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float nmb[2] = {0.f, 0.f};
-  float thr[2] = {INFINITY, INFINITY};
+  float m_ref = -INFINITY, nmb = 0.f, thr = INFINITY;
   bool ref_pending = true;
-  float l_part[2];
-  f32x16 acc[4][4];
+  float l_part;
+  f32x16 acc[kR / 32];
 
-  // ---- softmax pieces of one tile (scores s0, s1 of tile `it`) ----
-  float x[2][4], mxl[2];
-  float (&pr)[2][4] = x;  // probabilities overwrite the masked scores
+  // ---- softmax of one step (scores S of step it) -> value operands pv[2] ----
+  float x[16];
+  float mxl = -INFINITY;
   bool grow = false;
-  auto sm_mask = [&](int nb, const f32x4& s, int it) {
-    const int rel = dd[nb] - kTile * it;
+  auto sm_load = [&](const f32x16& S) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[nb][r] = (r < rel) ? s[r] : -INFINITY;
+    for (int r = 0; r < 16; ++r) x[r] = S[r];
+  };
+  auto sm_mask = [&](int it) {
+    const int rel = dd - kStepTok * it;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (8 * (r >> 2) + (r & 3) < rel) ? x[r] : -INFINITY;
   };
   auto sm_check = [&]() {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mxl[nb] = max4(x[nb][0], x[nb][1], x[nb][2], x[nb][3]);
-    grow = __builtin_amdgcn_ballot_w64((mxl[0] > thr[0]) | (mxl[1] > thr[1])) != 0;
+    const float m0 = max4(x[0], x[1], x[2], x[3]), m1 = max4(x[4], x[5], x[6], x[7]);
+    const float m2 = max4(x[8], x[9], x[10], x[11]), m3 = max4(x[12], x[13], x[14], x[15]);
+    mxl = max4(m0, m1, m2, m3);
+    grow = __builtin_amdgcn_ballot_w64(mxl > thr) != 0;
   };
-  auto sm_reference = [&]() {  // first visible tile of a row: fix m_ref
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float mx = max4lanes(max4(x[nb][0], x[nb][1], x[nb][2], x[nb][3]));
-      if (m_ref[nb] == -INFINITY && mx != -INFINITY) {
-        m_ref[nb] = mx * sl2;
-        nmb[nb] = -m_ref[nb];
-        thr[nb] = mx + lazy_raw;
-      }
+  auto sm_reference = [&]() {  // first visible step of a row: fix m_ref
+    float a, c;
+    xpair32(mxl, a, c);
+    const float mx = fmaxf(a, c);
+    if (m_ref == -INFINITY && mx != -INFINITY) {
+      m_ref = mx * sl2;
+      nmb = -m_ref;
+      thr = mx + lazy_raw;
     }
-    ref_pending = __builtin_amdgcn_ballot_w64((m_ref[0] == -INFINITY) | (m_ref[1] == -INFINITY)) != 0;
+    ref_pending = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;
   };
-  auto sm_fma = [&](int nb) {
+  auto sm_exp = [&](int r0, int r1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[nb][r] = __builtin_fmaf(x[nb][r], sl2, nmb[nb]);
-  };
-  auto sm_exp = [&](int nb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[nb][r] = __builtin_amdgcn_exp2f(pr[nb][r]);
+    for (int r = r0; r < r1; ++r) x[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], sl2, nmb));
   };
   auto sm_sum = [&]() {
+    float s = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) l_part[nb] += (pr[nb][0] + pr[nb][1]) + (pr[nb][2] + pr[nb][3]);
+    for (int r = 0; r < 16; r += 4) s += (x[r] + x[r + 1]) + (x[r + 2] + x[r + 3]);
+    l_part += s;
   };
-  // Probabilities to bf16, then one row exchange turns the score layout (lane:
-  // row (l&15) + 16nb, tokens 4(l>>4)..+3) into 8 consecutive tokens of one row
-  // per lane (row l & 31, tokens 8(l>>5)..+7), stored with one 16-byte write.
-  auto sm_store = [&](int it) {
-    const uint32_t base = pbuf_lds + (it & 1) * (kRowsPerWG * kTile * 2);
-    u32x2 a = cvt_bf16x4(f32x4{pr[0][0], pr[0][1], pr[0][2], pr[0][3]});
-    u32x2 c = cvt_bf16x4(f32x4{pr[1][0], pr[1][1], pr[1][2], pr[1][3]});
-    uint32_t a0 = a[0], a1 = a[1], c0 = c[0], c1 = c[1];
-    swap16(a0, c0);
-    swap16(a1, c1);
-    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(base + p_wr) = u32x4{a0, a1, c0, c1};
+  auto sm_pack = [&](bf16x8 (&pv)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x2 lo = cvt_bf16x4(f32x4{x[8 * kb], x[8 * kb + 1], x[8 * kb + 2], x[8 * kb + 3]});
+      const u32x2 hi = cvt_bf16x4(f32x4{x[8 * kb + 4], x[8 * kb + 5], x[8 * kb + 6], x[8 * kb + 7]});
+      pv[kb] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
   };
   // a row's max grew by more than kLazy: raise its reference, flag a replay
   auto sm_grow = [&]() {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float mx = max4lanes(mxl[nb]);
-      if (mx > thr[nb]) {
-        m_ref[nb] = mx * sl2;
-        nmb[nb] = -m_ref[nb];
-        thr[nb] = mx + lazy_raw;
-      }
+    float a, c;
+    xpair32(mxl, a, c);
+    const float mx = fmaxf(a, c);
+    if (mx > thr) {
+      m_ref = mx * sl2;
+      nmb = -m_ref;
+      thr = mx + lazy_raw;
     }
     if (l == 0) flag_s = 1u;
   };
-  // whole softmax of one tile, not interleaved (first tile, rows still without
-  // a reference)
-  auto softmax_tile = [&](const f32x4& s0, const f32x4& s1, int it) {
-    sm_mask(0, s0, it);
-    sm_mask(1, s1, it);
-    if (ref_pending) sm_reference();
+  // whole softmax of one step, not interleaved (prologue)
+  auto softmax_step = [&](const f32x16& S, int it, bf16x8 (&pv)[2]) {
+    sm_load(S);
+    sm_mask(it);
     sm_check();
-    sm_fma(0);
-    sm_fma(1);
-    sm_exp(0);
-    sm_exp(1);
+    if (ref_pending) sm_reference();
+    sm_exp(0, 16);
     sm_sum();
-    sm_store(it);
+    sm_pack(pv);
     if (grow) sm_grow();
   };
 
-  // scores S^T of tile `it` (not interleaved: prologue)
-  auto scores_plain = [&](int it, f32x4& s0, f32x4& s1) {
-    const uint32_t kbase = tiles_lds + (it % NB) * kTileBytes + k_lane;
-    s0 = f32x4{};
-    s1 = f32x4{};
+  // scores of step it, not interleaved (prologue)
+  auto scores_plain = [&](int it, f32x16& S) {
+    const uint32_t kbuf = tiles_lds + (it % NB) * kStepBytes;
+    const uint32_t kbase[2] = {opaque(kbuf + k_lane[0]), opaque(kbuf + k_lane[1])};
+    S = f32x16{};
     constexpr int PF = 4;
     bf16x8 kb[PF];
 #pragma unroll
-    for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
+    for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase[ks & 1] + 512 * ks);
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
+    for (int ks = 0; ks < kQk; ++ks) {
       const bf16x8 kop = kb[ks % PF];
-      if (ks + PF < 18) kb[ks % PF] = lds_b128(kbase + 1024 * (ks + PF));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], s1, 0, 0, 0);
+      if (ks + PF < kQk) kb[ks % PF] = lds_b128(kbase[(ks + PF) & 1] + 512 * (ks + PF));
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[ks], S, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Smallest key limit over this wave's rows: a tile ending at or before it
+  // V operand of value MFMA v from the step whose buffer bases are vb
+  // (buffer + v_lane[0], buffer + v_lane[1])
+  auto v_bases = [&](int it, uint32_t (&vb)[2]) {
+    const uint32_t buf = tiles_lds + (it % NB) * kStepBytes;
+    vb[0] = opaque(buf + v_lane[0]);
+    vb[1] = opaque(buf + v_lane[1]);
+  };
+  auto v_read = [&](const uint32_t (&vb)[2], int v) -> bf16x8 {
+    const uint32_t off = (v >> 4) * kTileBytes + 1024 * (v & 15);
+    return join8(lds_tr16(vb[0] + off), lds_tr16(vb[1] + off));
+  };
+
+  // Smallest key limit over this wave's rows: a step ending at or before it
   // needs no mask for any of them.
   int lim_lo = j1;
   {
@@ -458,150 +483,120 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     if (g0 < TH) lim_lo = min(L - T + g0 / H + 1, j1);
   }
 
+  constexpr int PF = 4;   // K operand reads in flight
+  constexpr int VPF = 4;  // V operands in flight
+
   // At most one replay: after a flagged pass every row's reference is within
   // kLazy of its true maximum, so the replay cannot flag again.
   for (int pass = 0;; ++pass) {
-    if (pg_base != j0 / P) {  // a replay after the page window moved: rewind it
-      pg_base = j0 / P;
-      const int pg = pg_base + l;
-      pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
+    if (pass > 0) {
+      dma_reset();
+      load_window(dma_page);
       __builtin_amdgcn_s_waitcnt(0);
     }
-    l_part[0] = l_part[1] = 0.f;
+    l_part = 0.f;
 #pragma unroll
-    for (int xx = 0; xx < 4; ++xx)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[xx][y] = f32x16{};
-    for (int it = 0; it < NB - 1 && it < ntiles; ++it) issue(it);
+    for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
+    if (nsteps > 0)
+      for (int it = 0; it < NB - 1; ++it) issue(it);
 
-    // Two-stage pipeline.  Step i (after its barrier): value MFMAs of tile i
-    // (probabilities P(i) written during step i-1), score MFMAs of tile i+2,
-    // and the softmax of tile i+1 (scores from step i-1) producing P(i+1).
-    // The first K operands of tile i+3 are read at the end of step i, so every
-    // step starts with MFMAs; tile i+3 has therefore landed before barrier i.
-    // Resident ring buffers: tiles i .. i+3; up to NB-5 more in flight.
-    constexpr int PF = 4;  // K operand reads in flight
-    bf16x8 kb[PF];
-    auto k_first = [&](int it) {
-      const uint32_t kbase = tiles_lds + (it % NB) * kTileBytes + k_lane;
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase + 1024 * ks);
-    };
-    f32x4 s0 = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, s1 = s0;  // scores of tile i+1
-    if (ntiles > 0) {
-      // prologue: tiles 0, 1 and 2 landed; P(0), the scores of tile 1 and the
-      // first K operands of tile 2
-      const int ahead = max(0, min(NB - 1, ntiles) - 3);
-      if (w < 2) wait_tiles<5, NB - 4>(ahead);
-      else wait_tiles<4, NB - 4>(ahead);
+    // One-stage pipeline.  Step i (after its barrier): value MFMAs of step i
+    // (probabilities pv from the softmax at the end of step i-1) interleaved
+    // with the score MFMAs of step i+1, then the softmax of step i+1 under the
+    // last value MFMAs.  Resident ring buffers: steps i and i+1; step i+2 in
+    // flight, step i+3 issued during the step (into the buffer of step i-1).
+    f32x16 S;
+    bf16x8 pv[2];
+    bf16x8 vop[VPF];
+    if (nsteps > 0) {
+      // prologue: step 0 landed; its scores and probabilities, first V operands
+      wait_vm<9 * (NB - 2)>();
       barrier();
-      clear_tail(0);
-      if (ntiles > 1) clear_tail(1);
-      if (ntiles > 2) clear_tail(2);
-      f32x4 t0, t1;
-      scores_plain(0, t0, t1);
-      softmax_tile(t0, t1, 0);
-      if (ntiles > 1) scores_plain(1, s0, s1);
-      k_first(2);
+      if (nsteps == 1 && j1 - j0 < kStepTok) {
+        clear_tail(0);
+        wait_lgkm0();
+        barrier();
+      }
+      scores_plain(0, S);
+      softmax_step(S, 0, pv);
+#pragma unroll
+      for (int v = 0; v < VPF; ++v) {
+        uint32_t vb[2];
+        v_bases(0, vb);
+        vop[v] = v_read(vb, v);
+      }
     }
-    for (int i = 0; i < ntiles; ++i) {
-      const bool do_qk = i + 2 < ntiles;
-      const bool do_sm = i + 1 < ntiles;
-      const bool do_issue = i + NB - 1 < ntiles;
-      // tile i+3 must have landed; up to NB-5 later tiles may stay in flight
-      if (i + 3 < ntiles) {
-        if (w < 2) wait_tiles<5, NB - 5>(min(NB - 5, ntiles - i - 4));
-        else wait_tiles<4, NB - 5>(min(NB - 5, ntiles - i - 4));
-      }
-      // this wave's probability writes and tail clears must be complete; LDS
-      // operations complete in order, so allowing only the PF K reads issued
-      // last (by k_first) to remain in flight is enough
-      wait_lgkm<PF>();
-      barrier();
-      if (i + 3 < ntiles) clear_tail(i + 3);
-      if (do_issue) issue_prep(i + NB - 1);
 
-      // softmax of tile i+1 done up front when some row still needs its
-      // reference; the interleaved copy below then runs on -inf scores, which
-      // makes every one of its steps a no-op (its probabilities are not stored)
-      bool sm_here = do_sm;
-      if (do_sm && ref_pending) {
-        softmax_tile(s0, s1, i + 1);
-        sm_here = false;
-        s0 = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        s1 = s0;
-      }
-      const bool full = j0 + kTile * (i + 2) <= lim_lo;  // tile i+1 needs no mask
-
-      const uint32_t kbase = tiles_lds + ((i + 2) % NB) * kTileBytes + k_lane;
-      const uint32_t pbase = pbuf_lds + (i & 1) * (kRowsPerWG * kTile * 2) + p_rd;
-      const uint32_t vbuf = tiles_lds + (i % NB) * kTileBytes + 4096 * w;
-      const uint32_t vb0 = vbuf + v_lane[0], vb1 = vbuf + v_lane[1];
-      bf16x8 pb[4], vop[2];
+    // body of step i (this wave's loads of step i+NB-1 are issued in it)
+    auto step = [&](int i) {
+      issue_prep(i + NB - 1);
+      const bool full = j0 + kStepTok * (i + 2) <= lim_lo;  // step i+1 needs no mask
+      // K of step i+1 (after the last step: a resident stale buffer, whose
+      // scores the mask discards)
+      const uint32_t kbuf = tiles_lds + ((i + 1) % NB) * kStepBytes;
+      const uint32_t kbase[2] = {opaque(kbuf + k_lane[0]), opaque(kbuf + k_lane[1])};
+      uint32_t vb_cur[2], vb_next[2];
+      v_bases(i, vb_cur);
+      v_bases(i + 1, vb_next);
+      bf16x8 kb[PF];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) pb[m] = lds_b128(pbase + 1024 * m);
-      vop[0] = join8(lds_tr16(vb0), lds_tr16(vb1));
-      // (the score MFMAs also run in the last two steps, on a stale buffer; their
-      // results are discarded)
-      f32x4 n0 = {}, n1 = {};  // scores of tile i+2
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        {
+      for (int ks = 0; ks < PF; ++ks) kb[ks] = lds_b128(kbase[ks & 1] + 512 * ks);
+      f32x16 Sn = {};
+      static_for<0, kSlots>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr Slot sl = slot_of(s);
+        if constexpr (sl.qk >= 0) {
+          constexpr int ks = sl.qk;
           const bf16x8 kop = kb[ks % PF];
-          if (ks + PF < 18) kb[ks % PF] = lds_b128(kbase + 1024 * (ks + PF));
-          n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[0][ks], n0, 0, 0, 0);
-          n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q[1][ks], n1, 0, 0, 0);
+          if constexpr (ks + PF < kQk) kb[ks % PF] = lds_b128(kbase[(ks + PF) & 1] + 512 * (ks + PF));
+          Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[ks], Sn, 0, 0, 0);
         }
-        // value MFMAs: none in steps 0-3 (their operands, read after the
-        // barrier, are still arriving), one per step in 4-13, two in 14-16
-        constexpr int kPvBegin[18] = {0, 0, 0, 0, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16};
-        constexpr int kPvEnd[18] = {0, 0, 0, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 14, 16, 16};
-#pragma unroll
-        for (int v = kPvBegin[ks]; v < kPvEnd[ks]; ++v) {
-          const int f = v >> 2, rb = v & 3;
-          mfma_pv(acc[f][rb], vop[f & 1], pb[rb]);
+        if constexpr (sl.pv >= 0) {
+          constexpr int v = sl.pv;
+          mfma_pv(acc[v & 15], vop[v % VPF], pv[v >> 4]);
+          // the V operand VPF value MFMAs ahead (the next step's first ones at the end)
+          if constexpr (v + VPF < kPv) vop[v % VPF] = v_read(vb_cur, v + VPF);
+          else vop[v % VPF] = v_read(vb_next, v + VPF - kPv);
         }
-        // V operand of column block f read a block ahead (two alternating slots)
-        if (ks == 2 || ks == 8 || ks == 12) {
-          const int f = ks == 2 ? 1 : ks == 8 ? 2 : 3;
-          vop[f & 1] = join8(lds_tr16(vb0 + 1024 * f), lds_tr16(vb1 + 1024 * f));
+        if constexpr (s < 8) issue_part(std::integral_constant<int, s>{});
+        if constexpr (s == 9) issue_part(std::integral_constant<int, 8>{});
+        // softmax of step i+1 (past the last step every score is masked)
+        if constexpr (s == 53) {
+          sm_load(Sn);
+          if (!full) sm_mask(i + 1);
         }
-        {
-          if (ks == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[0][r] = s0[r];
-            if (!full) sm_mask(0, s0, i + 1);
-          }
-          if (ks == 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[1][r] = s1[r];
-            if (!full) sm_mask(1, s1, i + 1);
-          }
-          if (ks == 2) sm_check();
-          if (ks == 3) sm_fma(0);
-          if (ks == 4) { pr[0][0] = __builtin_amdgcn_exp2f(pr[0][0]); pr[0][1] = __builtin_amdgcn_exp2f(pr[0][1]); }
-          if (ks == 5) { pr[0][2] = __builtin_amdgcn_exp2f(pr[0][2]); pr[0][3] = __builtin_amdgcn_exp2f(pr[0][3]); }
-          if (ks == 6) sm_fma(1);
-          if (ks == 7) { pr[1][0] = __builtin_amdgcn_exp2f(pr[1][0]); pr[1][1] = __builtin_amdgcn_exp2f(pr[1][1]); }
-          if (ks == 8) { pr[1][2] = __builtin_amdgcn_exp2f(pr[1][2]); pr[1][3] = __builtin_amdgcn_exp2f(pr[1][3]); }
-          if (ks == 9) sm_sum();
-          if (ks == 10 && sm_here) sm_store(i + 1);
+        if constexpr (s == 54) sm_check();
+        if constexpr (s == 55) {
+          if (ref_pending) sm_reference();
         }
-        if (do_issue) {
-          if (ks == 2) issue_part(std::integral_constant<int, 0>{});
-          if (ks == 6) issue_part(std::integral_constant<int, 1>{});
-          if (ks == 10) issue_part(std::integral_constant<int, 2>{});
-          if (ks == 14) issue_part(std::integral_constant<int, 3>{});
-          if (ks == 17) issue_part(std::integral_constant<int, 4>{});
-        }
+        if constexpr (s == 56) sm_exp(0, 4);
+        if constexpr (s == 57) sm_exp(4, 8);
+        if constexpr (s == 59) sm_exp(8, 12);
+        if constexpr (s == 60) sm_exp(12, 16);
+        if constexpr (s == 61) sm_sum();
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
+      // probabilities of step i+1 (the value MFMAs of step i have read pv)
+      sm_pack(pv);
       if (grow) sm_grow();
-      k_first(i + 3);  // (a stale buffer near the end; never used then)
-      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      s0 = do_qk ? n0 : ninf;
-      s1 = do_qk ? n1 : ninf;
+    };
+
+    for (int i = 0; i < nsteps; ++i) {
+      // step i+1 must have landed; the NB-3 later steps may stay in flight
+      wait_vm<9 * (NB - 3)>();
+      // the VPF prefetched V operands of step i (2 reads each) may stay in flight
+      wait_lgkm<2 * VPF>();
+      barrier();
+      if (i + 2 == nsteps && j1 - (j0 + kStepTok * (i + 1)) < kStepTok) {
+        // the last step is partial: clear its rows past the end before any
+        // wave reads it (once per work unit)
+        clear_tail(i + 1);
+        wait_lgkm0();
+        barrier();
+      }
+      step(i);
     }
+    wait_vm0();  // the loads issued past the last step
     mfma_drain();
     wait_lgkm0();
     barrier();
@@ -614,63 +609,56 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     wait_lgkm0();
   }
 
-  // ---- finalize: row sums, lse, normalisation ----
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float ls = sum4lanes(l_part[nb]);
-    const int rl = 32 * w + 16 * nb + (l & 15);
-    const int gr = row0 + rl;
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    if ((l >> 4) == 0) {
-      inv_s[rl] = inv;
-      if (gr < TH) {
-        // lse in natural log: (m + log2(sum)) * ln 2
-        const float lse2 = (ls > 0.f) ? m_ref[nb] + __builtin_amdgcn_logf(ls) : -INFINITY;
-        const float lse_nat = lse2 * 0.69314718055994530942f;
-        if constexpr (SPLIT) {
-          p.part_lse[(size_t)slot * TH + gr] = lse_nat;
-        } else {
-          if (p.lse) p.lse[(size_t)b * TH + gr] = lse_nat;
-        }
-      }
+  // ---- finalize: row sums (lanes l and l ^ 32 hold halves of each row), lse ----
+  float ls;
+  {
+    float a, c;
+    xpair32(l_part, a, c);
+    ls = a + c;
+  }
+  const float inv = ls > 0.f ? 1.f / ls : 0.f;
+  if (hl == 0 && grow_ < TH) {
+    // lse in natural log: (m + log2(sum)) * ln 2
+    const float lse2 = (ls > 0.f) ? m_ref + __builtin_amdgcn_logf(ls) : -INFINITY;
+    const float lse_nat = lse2 * 0.69314718055994530942f;
+    if constexpr (SPLIT) {
+      p.part_lse[(size_t)slot * TH + grow_] = lse_nat;
+    } else {
+      if (p.lse) p.lse[(size_t)b * TH + grow_] = lse_nat;
     }
   }
-  wait_lgkm0();
-  barrier();
 
   // ---- store: the workgroup's rows [row0, row0 + 128) of its output are one
   // contiguous block (1 KB per row in bf16, 2 KB in fp32).  The normalised
-  // accumulators are staged through the (now idle) tile ring in row-major
+  // accumulators are staged through the (now idle) step ring in row-major
   // order, then written with 16-byte-per-lane contiguous stores.  Staging
   // swizzle: 16-byte chunk c of staged row r sits at chunk c ^ (r & 15); in the
   // bf16 layout the two 8-byte halves of a chunk are also swapped when bit 4 of
   // r is set (both make the staging writes and the reads conflict-free).
+  // Accumulator acc[cb] register 4 q4 + e holds column 32cb + 8q4 + 4hl + e of
+  // row 32w + (l & 31).
   const int n_rows = min(kRowsPerWG, TH - row0);
   char* const dst_base = (char*)(SPLIT ? p.part_out : p.out) + ((size_t)slot * TH + row0) * kR * (OUT_F32 ? 4 : 2);
   constexpr int kRowOut = kR * (OUT_F32 ? 4 : 2);      // bytes per output row
   constexpr int kStageRows = OUT_F32 ? 64 : 128;       // rows per staging round (128 KB)
-  static_assert(kStageRows * kRowOut <= kRingBytes, "staging block exceeds the tile ring");
+  static_assert(kStageRows * kRowOut <= kRingBytes, "staging block exceeds the ring");
 #pragma unroll
-  for (int half = 0; half < 128 / kStageRows; ++half) {
+  for (int round = 0; round < 128 / kStageRows; ++round) {
+    if ((32 * w) / kStageRows == round) {
+      const int r = 32 * w - round * kStageRows + (l & 31);  // staged row
 #pragma unroll
-    for (int rbl = 0; rbl < kStageRows / 32; ++rbl) {
-      const int rb = half * (kStageRows / 32) + rbl;
-      const int r = 32 * rbl + (l & 31);  // staged row
-      const float inv = inv_s[32 * rb + (l & 31)];
-#pragma unroll
-      for (int fbl = 0; fbl < 4; ++fbl) {
+      for (int cb = 0; cb < kR / 32; ++cb) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[fbl][rb][4 * q4 + e] * inv;
-          // columns 128w + 32fbl + 8q4 + 4(l>>5) + [0,4)
+          for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * q4 + e] * inv;
           if constexpr (OUT_F32) {
-            const int c = 32 * w + 8 * fbl + 2 * q4 + (l >> 5);
+            const int c = 8 * cb + 2 * q4 + hl;
             *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16)) = v;
           } else {
-            const int c = 16 * w + 4 * fbl + q4;
-            const int hh = (l >> 5) ^ ((r >> 4) & 1);
+            const int c = 4 * cb + q4;
+            const int hh = hl ^ ((r >> 4) & 1);
             lds_st64(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16) + 8 * hh, cvt_bf16x4(v));
           }
         }
@@ -678,16 +666,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     }
     wait_lgkm0();
     barrier();
-    const int rows_here = min(kStageRows, n_rows - half * kStageRows);
-    char* const dst = dst_base + (size_t)half * kStageRows * kRowOut;
+    const int rows_here = min(kStageRows, n_rows - round * kStageRows);
+    char* const dst = dst_base + (size_t)round * kStageRows * kRowOut;
     constexpr int kChunksPerRow = kRowOut / 16;
-    for (int x = threadIdx.x; x < rows_here * kChunksPerRow; x += 256) {
-      const int r = x / kChunksPerRow, c = x - r * kChunksPerRow;
+    for (int xx = threadIdx.x; xx < rows_here * kChunksPerRow; xx += 256) {
+      const int r = xx / kChunksPerRow, c = xx - r * kChunksPerRow;
       u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16));
       if (!OUT_F32 && ((r >> 4) & 1)) v = u32x4{v[2], v[3], v[0], v[1]};
       *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = v;
     }
-    if (half + 1 < 128 / kStageRows) barrier();
+    if (round + 1 < 128 / kStageRows) barrier();
   }
 }
 
@@ -779,7 +767,7 @@ static hipError_t launch_decode_t(const DecodeParams& prm, int grid, hipStream_t
 
 hipError_t launch_decode(const DecodeParams& prm, int max_units, bool split, bool out_f32,
                          hipStream_t st) {
-  constexpr int NB = 8;
+  constexpr int NB = 4;
   const int grid = ((max_units + 7) / 8) * 8;  // whole XCD rounds; extra workgroups exit
   if (split) {
     if (out_f32) return launch_decode_t<NB, true, true>(prm, grid, st);
