@@ -154,6 +154,14 @@ constexpr Slot slot_of(int s) {
 }
 // value MFMA v: token block kb = v >> 4 (16 tokens), column block cb = v & 15
 
+// slots at which this wave issues its 9 load instructions of a step
+constexpr int kDmaSlot0 = 0, kDmaStride = 7;
+constexpr int dma_part_at(int s) {
+  return (s >= kDmaSlot0 && (s - kDmaSlot0) % kDmaStride == 0 && (s - kDmaSlot0) / kDmaStride < 9)
+             ? (s - kDmaSlot0) / kDmaStride
+             : -1;
+}
+
 template <int NB, bool SPLIT, bool OUT_F32>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // step ring; after the last step it is reused to stage the 128 KB output block
@@ -558,8 +566,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           if constexpr (v + VPF < kPv) vop[v % VPF] = v_read(vb_cur, v + VPF);
           else vop[v % VPF] = v_read(vb_next, v + VPF - kPv);
         }
-        if constexpr (s < 8) issue_part(std::integral_constant<int, s>{});
-        if constexpr (s == 9) issue_part(std::integral_constant<int, 8>{});
+        if constexpr (dma_part_at(s) >= 0) issue_part(std::integral_constant<int, dma_part_at(s)>{});
         // softmax of step i+1 (past the last step every score is masked)
         if constexpr (s == 53) {
           sm_load(Sn);
