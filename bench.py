@@ -10,8 +10,10 @@ permutation, synthetic N(0,1) bf16 inputs and N(0,1/512) weights.
 Timing: W warm-up steps, then K steps between two device synchronisations.
 Three replicas of the cache and of the weights rotate from step to step so that
 the 256 MB last-level cache cannot serve a step's reads from the previous one.
-The decode kernel is also bracketed by HIP events on the launch stream to get
-its own duration, from which the roofline fraction is computed.
+K eager steps bracket the decode kernel with HIP events on the launch stream to
+get its own duration, from which the roofline fraction is computed; the chain
+throughput (`value`) then comes from K replays of the step captured as a HIP
+graph (one graph per replica; `--no-graph` times the eager launches instead).
 
 Prints one JSON line (rank 0, one GPU).
 """
@@ -97,6 +99,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the chain with eager launches instead of replaying a captured HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -165,6 +169,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # decode-kernel time: HIP events around the decode launch of eager steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -172,9 +177,35 @@ def main():
         step(i % R, evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+    eager_ms_per_step = (t1 - t0) * 1e3 / K
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_ms_avg = float(np.mean(dec_ms))
+
+    # whole chain: one captured HIP graph per cache replica (the four launches of
+    # a step as graph nodes), replayed back to back
+    ms_per_step = eager_ms_per_step
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(R):
+                step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / K
 
     if args.copy_calibration:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
@@ -229,6 +260,8 @@ def main():
             "decode_alg_flops": dec_flops,
             "decode_tflops": dec_flops / (dec_ms_avg * 1e-3) / 1e12,
             "decode_mfma_frac": dec_flops / (dec_ms_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "chain_launch": "eager" if args.no_graph else "hip_graph",
+            "chain_eager_ms_per_step": eager_ms_per_step,
             "chain_alg_bytes": chain_algorithmic(case, dec_bytes),
             "chain_TBps": chain_algorithmic(case, dec_bytes) / (ms_per_step * 1e-3) / 1e12,
         },

@@ -11,6 +11,8 @@
 // Products are computed transposed (D^T = W^T q^T and W_UV lat^T) so that the
 // MFMA accumulator layout gives each lane four consecutive output columns of
 // one row, stored as one 8- or 16-byte write.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,6 +23,10 @@ namespace mla {
 // is staged in LDS with a padded row stride and read transposed
 // (ds_read_b64_tr_b16) as the A operand W^T[32 c x 16 n]; wave w owns columns
 // [32w, 32w+32) of the block.  B operand q^T[16 n x 32 m] comes from global.
+// Every load of a chunk of 64 query rows is issued before the first wait (the
+// kernel is a few memory round trips long, so latency is what it costs): the
+// weight slice, then the query rows, whose indices are clamped to M-1 so the
+// loads need no branch; columns of D^T past M are computed and never stored.
 constexpr int kAbsStride = 144;  // bf16 elements per staged W row (128 + 16 pad)
 
 __global__ __launch_bounds__(256) void absorb_kernel(AbsorbParams p) {
@@ -29,14 +35,30 @@ __global__ __launch_bounds__(256) void absorb_kernel(AbsorbParams p) {
   const int h = blockIdx.x >> 2;
   const int cblk = blockIdx.x & 3;
   const int H = p.H, M = p.M;
-  // stage W_UK[h][n][cblk*128 .. +128]
+  // W_UK[h][n][cblk*128 .. +128]: 2048 chunks of 8 elements, 8 per thread
   const uint16_t* wsrc = p.w_uk + (size_t)h * kDN * kR + cblk * 128;
+  u32x4 wv[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int id = threadIdx.x + 256 * k;  // 2048 chunks of 8 elements
-    const int n = id >> 4, cc = id & 15;
-    const u32x4 v = *(const u32x4*)(wsrc + (size_t)n * kR + 8 * cc);
-    *(u32x4*)&wt[n * kAbsStride + 8 * cc] = v;
+    const int id = threadIdx.x + 256 * k;
+    wv[k] = *(const u32x4*)(wsrc + (size_t)(id >> 4) * kR + 8 * (id & 15));
+  }
+  // query rows of the first chunk: q^T operand of k-step ks for row m = lane & 31
+  bf16x8 bq[2][8];
+  auto load_q = [&](int m0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = min(m0 + 32 * mb + (l & 31), M - 1);
+      const uint16_t* qsrc = p.q_nope + ((size_t)m * H + h) * kDN + 8 * (l >> 5);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) bq[mb][ks] = *(const bf16x8*)(qsrc + 16 * ks);
+    }
+  };
+  load_q(0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int id = threadIdx.x + 256 * k;
+    *(u32x4*)&wt[(id >> 4) * kAbsStride + 8 * (id & 15)] = wv[k];
   }
   __syncthreads();
   // A operands for the 8 k-steps: lane gets column c = 32w + (l & 31), rows
@@ -58,23 +80,25 @@ __global__ __launch_bounds__(256) void absorb_kernel(AbsorbParams p) {
       A[ks] = join8(x[0], x[1]);
     }
   }
-  for (int mb = 0; mb * 32 < M; ++mb) {
-    const int m = mb * 32 + (l & 31);
-    f32x16 acc = {};
-    const uint16_t* qsrc = p.q_nope + ((size_t)m * H + h) * kDN + 8 * (l >> 5);
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 bq = (m < M) ? *(const bf16x8*)(qsrc + 16 * ks) : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], bq, acc, 0, 0, 0);
-    }
-    if (m < M) {
-      uint16_t* dst = p.q_lat + ((size_t)m * H + h) * kR + cblk * 128 + 32 * w + 4 * (l >> 5);
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[4 * q4 + 0], acc[4 * q4 + 1]);
-        pk[1] = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
-        *(u32x2*)(dst + 8 * q4) = pk;
+      for (int ks = 0; ks < 8; ++ks)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], bq[mb][ks], acc[mb], 0, 0, 0);
+    if (m0 + 64 < M) load_q(m0 + 64);
+    // D^T lane layout: row m = m0 + 32mb + (l & 31), columns 32w + 8q4 + 4(l>>5) + e
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = m0 + 32 * mb + (l & 31);
+      if (m < M) {
+        uint16_t* dst = p.q_lat + ((size_t)m * H + h) * kR + cblk * 128 + 32 * w + 4 * (l >> 5);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v = {acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
+          *(u32x2*)(dst + 8 * q4) = cvt_bf16x4(v);
+        }
       }
     }
   }
@@ -90,7 +114,8 @@ hipError_t launch_absorb(const AbsorbParams& prm, hipStream_t st) {
 // Workgroup = (head h, 32-row block of v).  Wave w contracts c in
 // [128w, 128w+128): A = W_UV[h][32 v x 16 c] and B = lat^T[16 c x 32 m] both
 // come straight from global memory (16 contiguous bytes per lane); the four
-// partial sums are added through LDS.
+// partial sums are added through LDS.  As in the absorb kernel, all loads of a
+// 64-row chunk are issued before the first wait, with row indices clamped.
 template <bool LAT_F32>
 __global__ __launch_bounds__(256) void unabsorb_kernel(UnabsorbParams p) {
   __shared__ __attribute__((aligned(16))) float red[4][64 * 32];
@@ -105,45 +130,59 @@ __global__ __launch_bounds__(256) void unabsorb_kernel(UnabsorbParams p) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) A[ks] = *(const bf16x8*)(wsrc + 16 * ks);
   }
+  // latent^T operands of a 64-row chunk (fp32 latent: two 16-byte loads per operand)
+  typedef typename std::conditional<LAT_F32, f32x4, bf16x8>::type raw_t;
+  raw_t raw[2][8][LAT_F32 ? 2 : 1];
+  auto load_lat = [&](int m0) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int m = min(m0 + 32 * mb + (l & 31), M - 1);
+      const size_t row = ((size_t)m * H + h) * kR + 128 * w + 8 * (l >> 5);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if constexpr (LAT_F32) {
+          const float* src = (const float*)p.latent + row + 16 * ks;
+          raw[mb][ks][0] = *(const f32x4*)src;
+          raw[mb][ks][LAT_F32 ? 1 : 0] = *(const f32x4*)(src + 4);
+        } else {
+          raw[mb][ks][0] = *(const bf16x8*)((const uint16_t*)p.latent + row + 16 * ks);
+        }
+      }
+    }
+  };
+  load_lat(0);
   for (int m0 = 0; m0 < M; m0 += 64) {
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int m = m0 + 32 * mb + (l & 31);
-      if (m0 + 32 * mb >= M) break;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int c = 128 * w + 16 * ks + 8 * (l >> 5);
-        bf16x8 bl = {};
-        if (m < M) {
-          if constexpr (LAT_F32) {
-            const float* src = (const float*)p.latent + ((size_t)m * H + h) * kR + c;
-            bl = pack8(*(const f32x4*)src, *(const f32x4*)(src + 4));
-          } else {
-            bl = *(const bf16x8*)((const uint16_t*)p.latent + ((size_t)m * H + h) * kR + c);
-          }
-        }
+        bf16x8 bl;
+        if constexpr (LAT_F32) bl = pack8(raw[mb][ks][0], raw[mb][ks][LAT_F32 ? 1 : 0]);
+        else bl = raw[mb][ks][0];
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[ks], bl, acc[mb], 0, 0, 0);
       }
     }
+    if (m0 + 64 < M) load_lat(m0 + 64);
     // D^T lane layout: row m = 32mb + (l & 31), column v = 8(r>>2) + 4(l>>5) + (r&3)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vv = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-        red[w][(32 * mb + (l & 31)) * 32 + vv] = acc[mb][r];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 s = {acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
+        *(f32x4*)&red[w][(32 * mb + (l & 31)) * 32 + 8 * q4 + 4 * (l >> 5)] = s;
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int id = threadIdx.x + 256 * k;  // (mloc, vv)
-      const int mloc = id >> 5, vv = id & 31;
+    for (int k = 0; k < 2; ++k) {
+      const int id = threadIdx.x + 256 * k;  // (mloc, 4-column group)
+      const int mloc = id >> 3, vq = id & 7;
       const int m = m0 + mloc;
       if (m < M) {
-        const float s = red[0][id] + red[1][id] + red[2][id] + red[3][id];
-        p.out[((size_t)m * H + h) * kDV + 32 * vblk + vv] = s;
+        const f32x4 s = *(const f32x4*)&red[0][mloc * 32 + 4 * vq] + *(const f32x4*)&red[1][mloc * 32 + 4 * vq] +
+                        *(const f32x4*)&red[2][mloc * 32 + 4 * vq] + *(const f32x4*)&red[3][mloc * 32 + 4 * vq];
+        *(f32x4*)(p.out + ((size_t)m * H + h) * kDV + 32 * vblk + 4 * vq) = s;
       }
     }
     __syncthreads();

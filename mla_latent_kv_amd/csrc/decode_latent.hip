@@ -225,26 +225,20 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   // ---- this lane's query row (lanes l and l ^ 32 share it) ----
   // q[ks] holds elements 16ks + 8hl .. +7 of [q~ || q_pe] (the B operand of the
-  // score MFMA).  Key j of the row is visible iff j < lim; padding rows past
-  // T*H get a zero query and see every key (their scores are 0, never stored).
+  // score MFMA).  Key j of the row is visible iff j < lim.  Padding rows past
+  // T*H load the query of the last real row (so every load is unconditional),
+  // see every key of the range and are never stored.
   const int rloc = 32 * w + (l & 31);
   const int grow_ = row0 + rloc;
   bf16x8 q[kQk];
   int lim = j1;
-  if (grow_ < TH) {
-    const int t = grow_ / H;
-    const int h = grow_ - t * H;
-    lim = min(L - T + t + 1, j1);
-    const uint16_t* ql = p.q_lat + ((size_t)(b * T + t) * H + h) * kR + 8 * hl;
-    const uint16_t* qp = p.q_pe + ((size_t)(b * T + t) * H + h) * kDR + 8 * hl;
-#pragma unroll
-    for (int ks = 0; ks < kR / 16; ++ks) q[ks] = *(const bf16x8*)(ql + 16 * ks);
-#pragma unroll
-    for (int ks = 0; ks < kDR / 16; ++ks) q[kR / 16 + ks] = *(const bf16x8*)(qp + 16 * ks);
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < kQk; ++ks) q[ks] = bf16x8{};
+  const int qrow = min(grow_, TH - 1);
+  {
+    const int t = qrow / H;
+    if (grow_ < TH) lim = min(L - T + t + 1, j1);
   }
+  const uint16_t* ql = p.q_lat + ((size_t)b * TH + qrow) * kR + 8 * hl;
+  const uint16_t* qp = p.q_pe + ((size_t)b * TH + qrow) * kDR + 8 * hl;
   // score register r of step it is token j0 + 32 it + tok(r) + 4 hl with
   // tok(r) = 8 (r >> 2) + (r & 3): visible iff tok(r) < dd - 32 it
   const int dd = lim - j0 - 4 * hl;
@@ -277,10 +271,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   dma_reset();
   load_window(dma_page);
   if (threadIdx.x == 0) flag_s = 0u;
-  // q and the first page ids must be complete before any tile load is in flight:
-  // this wait is visible to the compiler, so it does not later wait for them
-  // against the (compiler-invisible) tile loads.
-  __builtin_amdgcn_s_waitcnt(0);
+  // The query rows are loaded after the page ids, so the compiler's wait for the
+  // page ids (at their first use) leaves the query loads in flight, overlapped
+  // with the first tile loads.  The score MFMAs of the first step consume all of
+  // q, so the compiler's waits for q all fall before the main loop (where a
+  // vector-memory wait would also drain the in-flight tile loads).
+#pragma unroll
+  for (int ks = 0; ks < kR / 16; ++ks) q[ks] = *(const bf16x8*)(ql + 16 * ks);
+#pragma unroll
+  for (int ks = 0; ks < kDR / 16; ++ks) q[kR / 16 + ks] = *(const bf16x8*)(qp + 16 * ks);
+  // consume the page ids here: the compiler's wait for them then counts the
+  // query loads behind them exactly
+  asm volatile("" ::"v"(pg_vec));
 
   const uint8_t* dma_base = cache;
   uint32_t dma_dst = 0;
@@ -496,17 +498,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   // At most one replay: after a flagged pass every row's reference is within
   // kLazy of its true maximum, so the replay cannot flag again.
-  for (int pass = 0;; ++pass) {
+  // An empty range (no key of the sequence in this unit) skips the pipeline:
+  // zero output and lse -inf.  Every path into the pipeline then passes through
+  // the first step's score MFMAs, which consume all of q, so the compiler's
+  // waits for the query loads never fall inside the main loop.
+  l_part = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
+  if (nsteps > 0) for (int pass = 0;; ++pass) {
     if (pass > 0) {
       dma_reset();
       load_window(dma_page);
       __builtin_amdgcn_s_waitcnt(0);
-    }
-    l_part = 0.f;
+      l_part = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
-    if (nsteps > 0)
-      for (int it = 0; it < NB - 1; ++it) issue(it);
+      for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
+    }
+    for (int it = 0; it < NB - 1; ++it) issue(it);
 
     // One-stage pipeline.  Step i (after its barrier): value MFMAs of step i
     // (probabilities pv from the softmax at the end of step i-1) interleaved
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     f32x16 S;
     bf16x8 pv[2];
     bf16x8 vop[VPF];
-    if (nsteps > 0) {
+    {
       // prologue: step 0 landed; its scores and probabilities, first V operands
       wait_vm<9 * (NB - 2)>();
       barrier();

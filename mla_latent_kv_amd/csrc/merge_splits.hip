@@ -8,9 +8,12 @@
 // merge of (m_r, l_r, o_r); mlxcel Stage 2 merge contract with normalised
 // partials).  Chunks with lse = -inf (no visible key) carry no weight.
 //
-// One wave per query row, 8 of the 512 columns per lane; the row's lse values
-// are wave-uniform scalar loads.  Partials are fp32 or bf16, accumulation is
-// fp32.  HBM-bound: every partial byte is read once, four partials in flight.
+// One wave per query row, 8 of the 512 columns per lane.  The row's lse values
+// are loaded one per lane (64 splits at a time), their maximum and weights are
+// formed with cross-lane reductions, and each split's weight is broadcast from
+// its lane while the partial rows stream in, eight in flight per wave (indices
+// past the row's last split are clamped and carry weight 0).  Partials are fp32
+// or bf16, accumulation is fp32.  HBM-bound: every partial byte is read once.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,6 +37,17 @@ __device__ __forceinline__ void load8(const void* base, size_t elem, f32x4& lo, 
   }
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <bool PART_F32, bool OUT_F32>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int w = wave_id(), l = lane_id();
@@ -47,35 +61,34 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const float* lse_col = p.part_lse + gr;
 
   float M = -INFINITY;
-  for (int k = k0; k < k1; ++k) M = fmaxf(M, lse_col[(size_t)k * TH]);
+  for (int k = k0 + l; k < k1; k += 64) M = fmaxf(M, lse_col[(size_t)k * TH]);
+  M = wave_max(M);
   float wsum = 0.f;
   f32x4 a0 = {}, a1 = {};
   if (M != -INFINITY) {
-    int k = k0;
-    for (; k + 4 <= k1; k += 4) {
-      f32x4 v[4][2];
-      float wk[4];
+    for (int kc = k0; kc < k1; kc += 64) {
+      // weight of split kc + l in lane l
+      const int kl = kc + l;
+      const float x = kl < k1 ? lse_col[(size_t)kl * TH] : -INFINITY;
+      const float wl = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
+      wsum += wave_sum(wl);
+      const int n = min(64, k1 - kc);
+      for (int u0 = 0; u0 < n; u0 += 8) {
+        f32x4 v[8][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        load8<PART_F32>(p.part_out, ((size_t)(k + u) * TH + gr) * kR + 8 * l, v[u][0], v[u][1]);
-        const float x = lse_col[(size_t)(k + u) * TH];
-        wk[u] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
-      }
+        for (int u = 0; u < 8; ++u) {
+          const int k = kc + min(u0 + u, n - 1);
+          load8<PART_F32>(p.part_out, ((size_t)k * TH + gr) * kR + 8 * l, v[u][0], v[u][1]);
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wsum += wk[u];
-        a0 += wk[u] * v[u][0];
-        a1 += wk[u] * v[u][1];
+        for (int u = 0; u < 8; ++u) {
+          const float wk = (u0 + u < n) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                   __builtin_bit_cast(int, wl), u0 + u))
+                                        : 0.f;
+          a0 += wk * v[u][0];
+          a1 += wk * v[u][1];
+        }
       }
-    }
-    for (; k < k1; ++k) {
-      f32x4 v0, v1;
-      load8<PART_F32>(p.part_out, ((size_t)k * TH + gr) * kR + 8 * l, v0, v1);
-      const float x = lse_col[(size_t)k * TH];
-      const float wk = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((x - M) * kLog2e);
-      wsum += wk;
-      a0 += wk * v0;
-      a1 += wk * v1;
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

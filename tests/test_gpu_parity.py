@@ -47,6 +47,8 @@ def small_cases():
         # starts at 32 = L - T + 1, where query t=0 sees none of its keys
         "mtp_p16_tail": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, page_size=16, lengths=(35, 51),
                                      seed=2108),
+        # 70 query tokens (B*T): the weight GEMMs take a second, partial 64-row chunk
+        "m70_h2": synth.scaled(W["v3_b64_l4096"], B=35, T=2, H=2, L=40, seed=2109),
     }
 
 
