@@ -135,23 +135,26 @@ __device__ __forceinline__ int tile_swz(int c) { return (-4 * c) & 12; }
 __device__ __forceinline__ int tile_pos(int c, int t) { return 16 * c + (t ^ tile_swz(c & 3)); }
 
 // ---- stream schedule of one step: 68 MFMA slots ----
-// slots 0-7: value MFMAs v = 0..7; slots 8-51: score MFMAs ks = 0..35 with value
-// MFMAs v = 8..15 after every fourth score MFMA; slots 52-67: value MFMAs
-// v = 16..31, under which the softmax of the next step runs.
+// slots 0-3: value MFMAs v = 0..3; slots 4-43: the 36 score MFMAs ks = 0..35
+// with value MFMAs v = 4..7 after every ninth; slots 44-67: value MFMAs
+// v = 8..31.  The softmax of the next step (about 70 vector instructions, 16
+// of them quarter-rate exponentials) is spread over slots 45-64, so that it
+// fits in the vector-ALU time the matrix core leaves free.
 struct Slot {
   int qk;  // score MFMA k-step or -1
   int pv;  // value MFMA index or -1
 };
 constexpr int kSlots = kQk + kPv;
 constexpr Slot slot_of(int s) {
-  if (s < 8) return Slot{-1, s};
-  if (s < 52) {
-    const int x = s - 8;  // 44 slots: pattern Q Q Q Q P (x8), then Q Q Q Q
-    if (x < 40) return (x % 5 == 4) ? Slot{-1, 8 + x / 5} : Slot{x / 5 * 4 + x % 5, -1};
-    return Slot{32 + (x - 40), -1};
+  if (s < 4) return Slot{-1, s};
+  if (s < 44) {
+    const int x = s - 4;  // 40 slots: nine score MFMAs, then one value MFMA (x4)
+    return (x % 10 == 9) ? Slot{-1, 4 + x / 10} : Slot{x / 10 * 9 + x % 10, -1};
   }
-  return Slot{-1, 16 + (s - 52)};
+  return Slot{-1, 8 + (s - 44)};
 }
+// softmax stages of the next step, by slot
+constexpr int kSmLoad = 45, kSmCheck = 46, kSmRef = 47, kSmExp0 = 48, kSmSum = 64, kSmPack = 65;
 // value MFMA v: token block kb = v >> 4 (16 tokens), column block cb = v & 15
 
 // slots at which this wave issues its 9 load instructions of a step
@@ -167,7 +170,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // step ring; after the last step it is reused to stage the 128 KB output block
   constexpr int kRingBytes = NB * kStepBytes > 128 * 1024 ? NB * kStepBytes : 128 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kRingBytes];
-  __shared__ unsigned flag_s;
+  // probabilities of all 128 rows, two steps: [step & 1][kb][row block][lane] x 16 B
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * 2 * 4 * 64 * 16];
 
   const int w = wave_id();
   const int l = lane_id();
@@ -270,7 +274,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   };
   dma_reset();
   load_window(dma_page);
-  if (threadIdx.x == 0) flag_s = 0u;
   // The query rows are loaded after the page ids, so the compiler's wait for the
   // page ids (at their first use) leaves the query loads in flight, overlapped
   // with the first tile loads.  The score MFMAs of the first step consume all of
@@ -380,6 +383,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // which a replay is needed; nmb = -m_ref (0 while the row has no visible key).
   float m_ref = -INFINITY, nmb = 0.f, thr = INFINITY;
   bool ref_pending = true;
+  bool grew = false;  // this wave raised a reference in the current pass
   float l_part;
   f32x16 acc[kR / 32];
 
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       nmb = -m_ref;
       thr = mx + lazy_raw;
     }
-    if (l == 0) flag_s = 1u;
+    grew = true;
   };
   // whole softmax of one step, not interleaved (prologue)
   auto softmax_step = [&](const f32x16& S, int it, bf16x8 (&pv)[2]) {
@@ -475,14 +479,27 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   // V operand of value MFMA v from the step whose buffer bases are vb
   // (buffer + v_lane[0], buffer + v_lane[1])
+  // (this wave's value columns are [128w, 128w + 128): column blocks 4w .. 4w+3)
   auto v_bases = [&](int it, uint32_t (&vb)[2]) {
-    const uint32_t buf = tiles_lds + (it % NB) * kStepBytes;
+    const uint32_t buf = tiles_lds + (it % NB) * kStepBytes + 4096 * w;
     vb[0] = opaque(buf + v_lane[0]);
     vb[1] = opaque(buf + v_lane[1]);
   };
-  auto v_read = [&](const uint32_t (&vb)[2], int v) -> bf16x8 {
-    const uint32_t off = (v >> 4) * kTileBytes + 1024 * (v & 15);
+  auto v_read = [&](const uint32_t (&vb)[2], int kb, int cb) -> bf16x8 {
+    const uint32_t off = kb * kTileBytes + 1024 * cb;
     return join8(lds_tr16(vb[0] + off), lds_tr16(vb[1] + off));
+  };
+  // probability operands: this wave's rows go to LDS after each softmax; row
+  // block rb of token block kb of a step is read back by every wave
+  const uint32_t pbuf_lds = lds_addr_of(pbuf);
+  auto p_write = [&](int it, const bf16x8 (&pv)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(pbuf_lds + ((((it & 1) * 2 + kb) * 4 + w) * 64 + l) * 16) = pv[kb];
+  };
+  auto p_read = [&](int it, int kb, int ri) -> bf16x8 {
+    const int rb = (w + ri) & 3;
+    return lds_b128(pbuf_lds + ((((it & 1) * 2 + kb) * 4 + rb) * 64 + l) * 16);
   };
 
   // Smallest key limit over this wave's rows: a step ending at or before it
@@ -494,7 +511,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   }
 
   constexpr int PF = 4;   // K operand reads in flight
-  constexpr int VPF = 4;  // V operands in flight
 
   // At most one replay: after a flagged pass every row's reference is within
   // kLazy of its true maximum, so the replay cannot flag again.
@@ -523,7 +539,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     // flight, step i+3 issued during the step (into the buffer of step i-1).
     f32x16 S;
     bf16x8 pv[2];
-    bf16x8 vop[VPF];
+    bf16x8 vc[4];  // V operands of the current token block, column blocks 0..3
+    bf16x8 pp[3];  // probability operands of row blocks w+1 .. w+3
     {
       // prologue: step 0 landed; its scores and probabilities, first V operands
       wait_vm<9 * (NB - 2)>();
@@ -535,12 +552,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       }
       scores_plain(0, S);
       softmax_step(S, 0, pv);
+      p_write(0, pv);
+      uint32_t vb[2];
+      v_bases(0, vb);
 #pragma unroll
-      for (int v = 0; v < VPF; ++v) {
-        uint32_t vb[2];
-        v_bases(0, vb);
-        vop[v] = v_read(vb, v);
-      }
+      for (int cb = 0; cb < 4; ++cb) vc[cb] = v_read(vb, 0, cb);
     }
 
     // body of step i (this wave's loads of step i+NB-1 are issued in it)
@@ -568,39 +584,49 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, q[ks], Sn, 0, 0, 0);
         }
         if constexpr (sl.pv >= 0) {
+          // value MFMA v: token block kb, row block ri (rows of wave w + ri), column
+          // block cb; the own row block's probabilities come from registers
           constexpr int v = sl.pv;
-          mfma_pv(acc[v & 15], vop[v % VPF], pv[v >> 4]);
-          // the V operand VPF value MFMAs ahead (the next step's first ones at the end)
-          if constexpr (v + VPF < kPv) vop[v % VPF] = v_read(vb_cur, v + VPF);
-          else vop[v % VPF] = v_read(vb_next, v + VPF - kPv);
+          constexpr int kb = v >> 4, ri = (v >> 2) & 3, cb = v & 3;
+          if constexpr (ri == 0) mfma_pv(acc[4 * cb], vc[cb], pv[kb]);
+          else mfma_pv(acc[4 * cb + ri], vc[cb], pp[ri - 1]);
+          // next row block's probabilities, four MFMAs ahead
+          if constexpr (cb == 0 && ri < 3) pp[ri] = p_read(i, kb, ri + 1);
+          // after its last use, the V operand of the next token block (the next
+          // step's first block at the end)
+          if constexpr (ri == 3) {
+            if constexpr (kb == 0) vc[cb] = v_read(vb_cur, 1, cb);
+            else vc[cb] = v_read(vb_next, 0, cb);
+          }
         }
         if constexpr (dma_part_at(s) >= 0) issue_part(std::integral_constant<int, dma_part_at(s)>{});
         // softmax of step i+1 (past the last step every score is masked)
-        if constexpr (s == 53) {
+        if constexpr (s == kSmLoad) {
           sm_load(Sn);
           if (!full) sm_mask(i + 1);
         }
-        if constexpr (s == 54) sm_check();
-        if constexpr (s == 55) {
+        if constexpr (s == kSmCheck) sm_check();
+        if constexpr (s == kSmRef) {
           if (ref_pending) sm_reference();
         }
-        if constexpr (s == 56) sm_exp(0, 4);
-        if constexpr (s == 57) sm_exp(4, 8);
-        if constexpr (s == 59) sm_exp(8, 12);
-        if constexpr (s == 60) sm_exp(12, 16);
-        if constexpr (s == 61) sm_sum();
+        if constexpr (s >= kSmExp0 && s < kSmExp0 + 16) sm_exp(s - kSmExp0, s - kSmExp0 + 1);
+        if constexpr (s == kSmSum) sm_sum();
+        if constexpr (s == kSmPack) {
+          // probabilities of step i+1 (the value MFMAs of step i are past pv)
+          sm_pack(pv);
+          p_write(i + 1, pv);
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
-      // probabilities of step i+1 (the value MFMAs of step i have read pv)
-      sm_pack(pv);
       if (grow) sm_grow();
     };
 
     for (int i = 0; i < nsteps; ++i) {
       // step i+1 must have landed; the NB-3 later steps may stay in flight
       wait_vm<9 * (NB - 3)>();
-      // the VPF prefetched V operands of step i (2 reads each) may stay in flight
-      wait_lgkm<2 * VPF>();
+      // this wave's probability writes are done; the last two V operand reads
+      // (two LDS reads each) may stay in flight
+      wait_lgkm<4>();
       barrier();
       if (i + 2 == nsteps && j1 - (j0 + kStepTok * (i + 1)) < kStepTok) {
         // the last step is partial: clear its rows past the end before any
@@ -615,13 +641,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     mfma_drain();
     wait_lgkm0();
     barrier();
-    const bool replay = flag_s != 0u && pass == 0;
-    if (!replay) break;
-    // a flagged pass is discarded and replayed with the raised references
-    wait_vm0();
-    barrier();
-    if (threadIdx.x == 0) flag_s = 0u;
+    // replay decision: the waves' flags meet in the (now idle) ring
+    if (l == 0) *(__attribute__((address_space(3))) unsigned*)(uintptr_t)(tiles_lds + 4 * w) = grew ? 1u : 0u;
     wait_lgkm0();
+    barrier();
+    const u32x4 fl = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)tiles_lds;
+    wait_lgkm0();
+    barrier();  // every wave has read the flags before the ring is reused
+    if (!((fl[0] | fl[1] | fl[2] | fl[3]) != 0u && pass == 0)) break;
+    // a flagged pass is discarded and replayed with the raised references
+    grew = false;
   }
 
   // ---- finalize: row sums (lanes l and l ^ 32 hold halves of each row), lse ----
@@ -631,7 +660,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     xpair32(l_part, a, c);
     ls = a + c;
   }
-  const float inv = ls > 0.f ? 1.f / ls : 0.f;
+  // every wave stores all 128 rows (its 128 columns): the inverse row sums meet
+  // in the (now idle) probability buffer
+  if (hl == 0) *(__attribute__((address_space(3))) float*)(uintptr_t)(pbuf_lds + 4 * rloc) = ls > 0.f ? 1.f / ls : 0.f;
   if (hl == 0 && grow_ < TH) {
     // lse in natural log: (m + log2(sum)) * ln 2
     const float lse2 = (ls > 0.f) ? m_ref + __builtin_amdgcn_logf(ls) : -INFINITY;
@@ -650,8 +681,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // swizzle: 16-byte chunk c of staged row r sits at chunk c ^ (r & 15); in the
   // bf16 layout the two 8-byte halves of a chunk are also swapped when bit 4 of
   // r is set (both make the staging writes and the reads conflict-free).
-  // Accumulator acc[cb] register 4 q4 + e holds column 32cb + 8q4 + 4hl + e of
-  // row 32w + (l & 31).
+  // Accumulator acc[4cb + ri] register 4 q4 + e holds column
+  // 128w + 32cb + 8q4 + 4hl + e of row 32 rb + (l & 31), rb = (w + ri) & 3.
+  wait_lgkm0();
+  barrier();
+  float inv[4];
+#pragma unroll
+  for (int ri = 0; ri < 4; ++ri)
+    inv[ri] = *(const __attribute__((address_space(3))) float*)(uintptr_t)(pbuf_lds + 4 * (32 * ((w + ri) & 3) + (l & 31)));
   const int n_rows = min(kRowsPerWG, TH - row0);
   char* const dst_base = (char*)(SPLIT ? p.part_out : p.out) + ((size_t)slot * TH + row0) * kR * (OUT_F32 ? 4 : 2);
   constexpr int kRowOut = kR * (OUT_F32 ? 4 : 2);      // bytes per output row
@@ -659,20 +696,23 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   static_assert(kStageRows * kRowOut <= kRingBytes, "staging block exceeds the ring");
 #pragma unroll
   for (int round = 0; round < 128 / kStageRows; ++round) {
-    if ((32 * w) / kStageRows == round) {
-      const int r = 32 * w - round * kStageRows + (l & 31);  // staged row
 #pragma unroll
-      for (int cb = 0; cb < kR / 32; ++cb) {
+    for (int ri = 0; ri < 4; ++ri) {
+      const int rb = (w + ri) & 3;
+      if ((32 * rb) / kStageRows != round) continue;
+      const int r = 32 * rb - round * kStageRows + (l & 31);  // staged row
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * q4 + e] * inv;
+          for (int e = 0; e < 4; ++e) v[e] = acc[4 * cb + ri][4 * q4 + e] * inv[ri];
           if constexpr (OUT_F32) {
-            const int c = 8 * cb + 2 * q4 + hl;
+            const int c = 32 * w + 8 * cb + 2 * q4 + hl;
             *(__attribute__((address_space(3))) f32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16)) = v;
           } else {
-            const int c = 4 * cb + q4;
+            const int c = 16 * w + 4 * cb + q4;
             const int hh = hl ^ ((r >> 4) & 1);
             lds_st64(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16) + 8 * hh, cvt_bf16x4(v));
           }
