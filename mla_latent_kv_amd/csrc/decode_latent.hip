@@ -266,7 +266,24 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     const int pg = base + l;
     pg_vec = (pg < p.max_blocks && pg * P < j1) ? bt_row[pg] : 0;
   };
-  int dma_page = 0, dma_off = 0;  // page and in-page row of this wave's next half-tile
+  // This wave's half of the next step to issue: page index, row in the page and
+  // the address of those rows, advanced step by step (a block-table lookup only
+  // when the half crosses into another page; page_size is a multiple of 16).
+  int dma_page = 0, dma_off = 0;
+  const uint8_t* dma_row = cache;
+  const uint32_t page_bytes = (uint32_t)P * kRowBytes;
+  auto page_ptr = [&](int page) -> const uint8_t* {
+    if (page < pg_base || page >= pg_base + 64) {
+      load_window(page);
+      // complete the reload here, visibly to the compiler, so that the common
+      // path carries no wait for it (a vector-memory wait would also drain the
+      // in-flight tile loads)
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    const uint32_t phys = (uint32_t)__builtin_amdgcn_readlane(pg_vec, page - pg_base);
+    return cache + (uint64_t)phys * page_bytes;
+  };
+  auto half_live = [&](int it) { return j0 + kStepTok * it + 16 * hw < j1; };
   auto dma_reset = [&]() {
     const int jt = j0 + 16 * hw;
     dma_page = jt / P;
@@ -286,46 +303,34 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // consume the page ids here: the compiler's wait for them then counts the
   // query loads behind them exactly
   asm volatile("" ::"v"(pg_vec));
+  auto dma_start = [&]() {
+    if (half_live(0)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRowBytes;
+  };
 
   const uint8_t* dma_base = cache;
   uint32_t dma_dst = 0;
-  // Loads of steps past the last one (the pipeline issues NB-1 steps ahead
-  // unconditionally) repeat the previous step's rows, which the L2 still holds,
-  // into the ring buffer that no wave reads any more; this keeps the issue
-  // path and the wait counts free of branches.
+  // A half past the end of the range (the second half of a short last step,
+  // and every load issued past the last step: the pipeline issues NB-1 steps
+  // ahead unconditionally) reads rows 0-15 of the cache, which are valid memory
+  // the L2 keeps; its rows are cleared or masked before any use, and no wave
+  // reads a buffer filled past the last step.  This keeps the issue path and
+  // the wait counts free of branches.
   auto issue_prep = [&](int it) {
-    if (it < nsteps) {
-      int page = dma_page, off = dma_off;
-      if (j0 + kStepTok * it + 16 * hw >= j1) {
-        // this half lies past the end: load the step's first half again (valid
-        // rows of a valid page); its rows are cleared before any use
-        off -= 16;
-        if (off < 0) {
-          off += P;
-          --page;
-        }
-      }
-      if (page < pg_base || page >= pg_base + 64) {
-        load_window(page);
-        // complete the reload here, visibly to the compiler, so that the common
-        // path carries no wait for it (a vector-memory wait would also drain the
-        // in-flight tile loads)
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      const int phys = __builtin_amdgcn_readlane(pg_vec, page - pg_base);
-      dma_base = cache + ((size_t)phys * P + off) * kRowBytes;
-      // advance to the same half of the next step (page_size is a multiple of 16)
-      dma_off += kStepTok;
+    dma_base = half_live(it) ? dma_row : cache;
+    dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
+    // advance to the same half of the next step
+    dma_off += kStepTok;
+    if (dma_off >= P) {
+      dma_off -= P;
+      ++dma_page;
       if (dma_off >= P) {
         dma_off -= P;
         ++dma_page;
-        if (dma_off >= P) {
-          dma_off -= P;
-          ++dma_page;
-        }
       }
+      if (half_live(it + 1)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRowBytes;
+    } else {
+      dma_row += kStepTok * kRowBytes;
     }
-    dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
   };
   auto issue_part = [&](auto n_const) {
     constexpr int n = decltype(n_const)::value;
@@ -526,6 +531,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       dma_reset();
       load_window(dma_page);
       __builtin_amdgcn_s_waitcnt(0);
+    }
+    dma_start();
+    if (pass > 0) {
       l_part = 0.f;
 #pragma unroll
       for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
