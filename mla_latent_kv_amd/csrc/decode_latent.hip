@@ -742,82 +742,129 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   }
 }
 
-// ---- split plan: work list (b, j0, j1, slot) and split_indptr ----
-// S > 0: every sequence cut into S chunks of ceil(ceil(L/S)/P)*P tokens.
-// S == 0: chunk = max(min_chunk, ceil(sum(L)/target_units) rounded up to P);
-//         S_b = clamp(ceil(L_b/chunk), 1, cap); chunk_b = ceil(ceil(L_b/S_b)/P)*P.
+// ---- automatic split plan: work list (b, j0, j1, slot) and split_indptr ----
+// One workgroup.  The decode launch runs one work unit per CU at a time, so its
+// time is set by the longest unit: the chunk length is the smallest multiple of
+// the page size (at least min_chunk) for which the units
+//     units(c) = sum_b clamp(ceil(L_b / c), 1, cap)
+// fit in target_units (the CU count).  With B < target_units the answer is at
+// most c = sum/(target - B) (each sequence rounding up by a whole unit, which
+// always fits) and at least min_chunk; two rounds of a search over that range,
+// 256 candidates a round (four threads per candidate, each counting a quarter
+// of the sequences), find it.  If one unit per sequence
+// already exceeds the target, every sequence is one unit.  A sequence's S_b
+// chunks are equal up to the page rounding: chunk_b = ceil(ceil(L_b/S_b)/P)*P.
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
-  __shared__ int red[1024];
-  __shared__ long long total_s;
+  constexpr int kLens = 4096;  // lengths cached in LDS (more are read from memory)
+  __shared__ int lens[kLens];
+  __shared__ int red_max, red_best;
+  __shared__ unsigned long long red_sum;
+  __shared__ int wave_tot[16];
+  __shared__ int cand_units[256];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int B = p.B, P = p.page_size;
-  const int per = (B + 1023) / 1024;
-  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-  int chunk_auto = 0;
-  if (p.num_splits == 0) {
-    long long sum = 0;
-    for (int b = b0; b < b1; ++b) sum += p.seqlens[b];
-    // block reduction of the total length
-    __shared__ long long sred[1024];
-    sred[tid] = sum;
-    __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-      if (tid < s) sred[tid] += sred[tid + s];
+  if (tid == 0) {
+    red_max = 0;
+    red_best = 0x7fffffff;
+    red_sum = 0ull;
+  }
+  __syncthreads();
+  int mx = 0;
+  unsigned long long sm = 0;
+  for (int b = tid; b < B; b += 1024) {
+    const int L = max(0, p.seqlens[b]);
+    if (b < kLens) lens[b] = L;
+    mx = max(mx, L);
+    sm += (unsigned)L;
+  }
+  // wave reductions first: same-address LDS atomics from every lane serialise
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o));
+    sm += __shfl_xor(sm, o);
+  }
+  if (lane == 0) {
+    atomicMax(&red_max, mx);
+    atomicAdd(&red_sum, sm);
+  }
+  __syncthreads();
+  auto len = [&](int b) { return b < kLens ? lens[b] : max(0, p.seqlens[b]); };
+  auto splits = [&](int L, unsigned chunk) {
+    const unsigned s = ((unsigned)L + chunk - 1u) / chunk;
+    return (int)max(1u, min((unsigned)p.cap, s));
+  };
+  const int kmax = max(1, (red_max + P - 1) / P);  // one unit per sequence
+  int kbest = kmax;
+  if (B < p.target_units) {
+    const unsigned long long tot = red_sum;
+    const int kmin = max(1, (p.min_chunk + P - 1) / P);
+    const unsigned long long per_hi = (tot + (unsigned long long)(p.target_units - B) * P - 1) /
+                                      ((unsigned long long)(p.target_units - B) * P);
+    int hi = (int)min((unsigned long long)kmax, max(per_hi, (unsigned long long)kmin));
+    int lo = min(kmin, hi);
+    for (int round = 0; round < 2 && lo < hi; ++round) {
+      const int step = (hi - lo + 256) / 256;  // ceil((hi - lo + 1) / 256)
+      // thread (candidate c, group g) counts the units of sequences b = g mod 4
+      const int c = tid & 255, g = tid >> 8;
+      const int k = min(hi, lo + c * step);
+      if (tid < 256) cand_units[tid] = 0;
+      __syncthreads();
+      int units = 0;
+      for (int b = g; b < B; b += 4) units += splits(len(b), (unsigned)k * (unsigned)P);
+      atomicAdd(&cand_units[c], units);
+      __syncthreads();
+      // smallest feasible candidate: per wave, then one atomic per wave
+      if (tid < 256) {
+        int kb = cand_units[tid] <= p.target_units ? k : 0x7fffffff;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) kb = min(kb, __shfl_xor(kb, o));
+        if (lane == 0) atomicMin(&red_best, kb);
+      }
+      __syncthreads();
+      const int best = min(red_best, hi);  // hi is feasible even when no candidate hit it
+      __syncthreads();
+      if (tid == 0) red_best = 0x7fffffff;
+      hi = best;
+      lo = max(lo, best - step + 1);
       __syncthreads();
     }
-    if (tid == 0) total_s = sred[0];
-    __syncthreads();
-    const long long tot = total_s;
-    long long c = (tot + p.target_units - 1) / p.target_units;
-    c = ((c + P - 1) / P) * P;
-    if (c < p.min_chunk) c = p.min_chunk;
-    chunk_auto = (int)c;
+    kbest = hi;
   }
-  // split count per sequence and local prefix
+  const unsigned chunk = (unsigned)kbest * (unsigned)P;
+  // split counts of this thread's contiguous range of sequences, and their prefix
+  const int per = (B + 1023) / 1024;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   int local = 0;
-  for (int b = b0; b < b1; ++b) {
-    int s;
-    if (p.num_splits > 0) s = p.num_splits;
-    else {
-      const int L = p.seqlens[b];
-      s = (L + chunk_auto - 1) / chunk_auto;
-      s = max(1, min(p.cap, s));
-    }
-    local += s;
+  for (int b = b0; b < b1; ++b) local += splits(len(b), chunk);
+  // exclusive scan over the 1024 threads: within each wave, then across waves
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
   }
-  red[tid] = local;
+  if (lane == 63) wave_tot[wv] = incl;
   __syncthreads();
-  // inclusive scan (Hillis-Steele) over 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = tid >= off ? red[tid - off] : 0;
-    __syncthreads();
-    red[tid] += v;
-    __syncthreads();
-  }
-  int base = red[tid] - local;
-  if (tid == 1023) *p.n_items = red[1023];
+  int before = 0;
+  for (int k = 0; k < wv; ++k) before += wave_tot[k];
+  int base = before + incl - local;
+  if (tid == 1023) *p.n_items = before + incl;
   if (tid == 0) p.split_indptr[0] = 0;
   for (int b = b0; b < b1; ++b) {
-    const int L = p.seqlens[b];
-    int s;
-    if (p.num_splits > 0) s = p.num_splits;
-    else {
-      s = (L + chunk_auto - 1) / chunk_auto;
-      s = max(1, min(p.cap, s));
-    }
-    const int per_s = (L + s - 1) / s;
-    const int chunk = ((per_s + P - 1) / P) * P;
-    for (int k = 0; k < s; ++k) {
-      long long a0 = (long long)k * chunk, a1 = a0 + chunk;
-      if (a0 > L) a0 = L;
-      if (a1 > L) a1 = L;
+    const int L = len(b);
+    const int sb = splits(L, chunk);
+    const int cb = ((L + sb - 1) / sb + P - 1) / P * P;
+    for (int k = 0; k < sb; ++k) {
+      const long long a0 = min((long long)L, (long long)k * cb);
+      const long long a1 = min((long long)L, a0 + cb);
       int* wi = p.work + 4 * (size_t)(base + k);
       wi[0] = b;
       wi[1] = (int)a0;
       wi[2] = (int)a1;
       wi[3] = base + k;
     }
-    base += s;
+    base += sb;
     p.split_indptr[b + 1] = base;
   }
 }
