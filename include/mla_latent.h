@@ -80,8 +80,13 @@ int mla_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, uint16_t* q_lat, 
  *   *workspace_bytes  -- bytes of the `workspace` argument (0 unless num_splits == 0);
  *   *max_total_splits -- rows of part_out / part_lse (0 when num_splits == 1).
  * num_splits: 1 = no split; S > 1 = every sequence cut into S chunks (see
- * mla_decode_latent); 0 = automatic (split counts chosen on the device from the
- * sequence lengths so that the work fills the GPU's compute units).
+ * mla_decode_latent); 0 = automatic, chosen on the device from the sequence
+ * lengths: with U = compute units / ceil(T*H/128) work units available at once,
+ * the chunk c is the smallest multiple of page_size, at least 256 tokens, with
+ *     sum_b clamp(ceil(L_b / c), 1, 128) <= U
+ * (every sequence one chunk when B >= U); sequence b is cut into
+ * S_b = clamp(ceil(L_b / c), 1, 128) chunks of ceil(ceil(L_b/S_b)/page_size)
+ * * page_size tokens (split_indptr[b+1] - split_indptr[b] = S_b).
  * Queries the current HIP device (compute-unit count) when num_splits == 0. */
 int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int page_size,
                               int num_splits, size_t* workspace_bytes, int* max_total_splits);

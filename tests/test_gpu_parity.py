@@ -283,3 +283,46 @@ def test_validate_inputs(mk):
     sl = case.seqlens.copy()
     sl[1] = case.max_seqlen + 1
     assert mk.mla_validate_inputs(d["block_table"], torch.from_numpy(sl).cuda(), *args) == -7
+
+
+@pytest.mark.parametrize("lengths,page", [
+    (None, 64),                                   # the ragged case above (5 sequences)
+    (tuple(range(100, 100 + 37 * 211, 211)), 64),  # 37 sequences, growing lengths
+    ((1, 16, 4000, 9000, 70000), 16),            # one very long sequence, small pages
+])
+def test_auto_split_counts(mk, lengths, page):
+    """The automatic split counts equal the rule the header states, evaluated
+    here by brute force over every page multiple: the smallest chunk c >= 256
+    with sum_b clamp(ceil(L_b/c), 1, 128) <= CUs."""
+    import torch
+    base = CASES["v3_ragged_b5"]
+    wl = base if lengths is None else synth.scaled(base, B=len(lengths), lengths=lengths, page_size=page,
+                                                   seed=2110)
+    case = synth.make_case(wl)
+    d = upload(case)
+    log(f"[split auto counts] B={case.B} page={case.page_size}")
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, 0, "cuda:0")
+    q_lat = bf16_tensor(_stage_q_lat(case, 7400), "cuda:0")
+    mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                         case.max_seqlen, SCALE, num_splits=0, buffers=buf, merge=False)
+    torch.cuda.synchronize()
+    counts = np.diff(buf.split_indptr.cpu().numpy())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    target = cus // ((case.T * case.H + 127) // 128)
+    L = case.seqlens.astype(np.int64)
+    P = case.page_size
+
+    def split(c):
+        return np.clip(-(-L // c), 1, 128)
+
+    kmax = max(1, -(-int(L.max()) // P))
+    if case.B >= target:
+        want = split(kmax * P)
+    else:
+        want = None
+        for k in range(-(-256 // P), max(-(-256 // P), kmax) + 1):
+            if split(k * P).sum() <= target:
+                want = split(k * P)
+                break
+    assert want is not None
+    assert np.array_equal(counts, want), (counts, want)
