@@ -14,7 +14,8 @@
 // are never normalised independently).
 //
 // Workgroup layout (256 threads = 4 waves of 64, one workgroup per CU).  Wave w
-// owns query rows [32w, 32w + 32) for the whole computation:
+// owns query rows [32w, 32w + 32) for the scores and the softmax, and latent
+// columns [128w, 128w + 128) of all 128 rows for the value GEMM:
 //  * KV rows stream HBM -> LDS with direct-to-LDS loads in steps of 32 tokens
 //    (two 16-row halves, 36 KB) into a ring of NB step buffers; waves 0-1 load
 //    the first half of every step, waves 2-3 the second.
@@ -27,19 +28,23 @@
 //    own scores against m_ref + kLazy; only when one exceeds it is m_ref
 //    raised and the work unit replayed from its first step (exact for any
 //    finite scores; never taken for scores of ordinary magnitude).
-//  * Values: O^T[512 cols x 32 rows] += V^T P^T with 32 32x32x16 MFMAs per step
-//    (256 accumulator registers).  The score accumulator layout is exactly the
-//    P^T operand layout (with the token order inside each 16-token block taken
-//    as the MFMA's k order and V read in the same order), so the
-//    probabilities never leave the registers; V comes from LDS through
-//    transposing reads (ds_read_b64_tr_b16).
+//  * Values: O^T[128 cols x 128 rows] += V^T P^T with 32 32x32x16 MFMAs per
+//    step (4 column blocks x 4 row blocks x 2 token blocks; 256 accumulator
+//    registers).  The score accumulator layout is exactly the P^T operand
+//    layout (with the token order inside each 16-token block taken as the
+//    MFMA's k order and V read in the same order): a wave uses its own rows'
+//    probabilities straight from registers and writes them to a 16 KB LDS
+//    double buffer for the other waves.  V comes from LDS through transposing
+//    reads (ds_read_b64_tr_b16), each operand read once and used for four row
+//    blocks.
 //  * Software pipeline, one barrier per 32-token step: the value MFMAs of step
-//    i and the score MFMAs of step i+1 form one MFMA stream; the softmax of
-//    step i+1 runs on the vector ALU under the last value MFMAs; LDS operand
-//    reads and this wave's load instructions for step i+NB-1 sit in between.
-//    A single wave per SIMD issues at most one instruction every four cycles,
-//    so the design keeps non-MFMA instructions few: about 330 per 32 tokens
-//    for 68 MFMAs (2176 matrix-core cycles).
+//    i and the score MFMAs of step i+1 form one MFMA stream (a compile-time
+//    slot table); the softmax of step i+1 runs on the vector ALU under the
+//    last value MFMAs; LDS operand reads and this wave's load instructions
+//    for step i+NB-1 sit in between.  With one wave per SIMD every non-MFMA
+//    instruction competes for the same issue slots, so the loop keeps them
+//    few (68 MFMAs, about 60 LDS, 160 vector and 60 scalar instructions per
+//    32 tokens).
 //
 // LDS layout of a 16-row half (chunk-major): the 16-byte chunk c (c < 72) of
 // row t is stored at chunk position 16c + (t ^ g(c & 3)), g = (0, 12, 8, 4).
@@ -57,7 +62,7 @@ constexpr float kLazy = 64.0f;               // log2-domain growth of the max to
 constexpr int kStepTok = 32;                 // tokens per pipeline step
 constexpr int kStepBytes = 2 * kTileBytes;   // two 16-row halves
 constexpr int kQk = kRow / 16;               // 36 score MFMAs per step (k = 16 each)
-constexpr int kPv = 2 * (kR / 32);           // 32 value MFMAs per step (2 token blocks x 16 column blocks)
+constexpr int kPv = 32;  // value MFMAs per wave and step (2 token blocks x 4 row blocks x 4 column blocks)
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -155,7 +160,8 @@ constexpr Slot slot_of(int s) {
 }
 // softmax stages of the next step, by slot
 constexpr int kSmLoad = 45, kSmCheck = 46, kSmRef = 47, kSmExp0 = 48, kSmSum = 64, kSmPack = 65;
-// value MFMA v: token block kb = v >> 4 (16 tokens), column block cb = v & 15
+// value MFMA v: token block kb = v >> 4 (16 tokens), row block ri = (v >> 2) & 3
+// (the rows of wave w + ri), this wave's column block cb = v & 3
 
 // slots at which this wave issues its 9 load instructions of a step
 constexpr int kDmaSlot0 = 0, kDmaStride = 7;
