@@ -62,14 +62,20 @@ def build(verbose: bool = False) -> str:
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the kernel and ABI sources (identifies which build a stored
-    counter measurement belongs to)."""
+    """sha256 over the kernel and ABI sources with comments and whitespace
+    removed (identifies which code a stored counter measurement belongs to;
+    editing a comment does not change it)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(name.encode())
+        h.update(text.encode())
     return h.hexdigest()
 
 
