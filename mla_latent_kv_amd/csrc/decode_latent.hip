@@ -62,7 +62,7 @@ constexpr float kLazy = 64.0f;               // log2-domain growth of the max to
 constexpr int kStepTok = 32;                 // tokens per pipeline step
 constexpr int kStepBytes = 2 * kTileBytes;   // two 16-row halves
 constexpr int kQk = kRow / 16;               // 36 score MFMAs per step (k = 16 each)
-constexpr int kPv = 32;  // value MFMAs per wave and step (2 token blocks x 4 row blocks x 4 column blocks)
+constexpr int kPv = 2 * (kR / 32);  // value MFMAs per wave and step (2 token blocks x 4 row blocks x 4 column blocks)
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
