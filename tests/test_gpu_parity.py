@@ -49,6 +49,12 @@ def small_cases():
                                      seed=2108),
         # 70 query tokens (B*T): the weight GEMMs take a second, partial 64-row chunk
         "m70_h2": synth.scaled(W["v3_b64_l4096"], B=35, T=2, H=2, L=40, seed=2109),
+        # the history lengths M5.8 0x0E's shape matrix names (around a 128-token
+        # boundary, a single key, a long history)
+        "history_matrix": synth.scaled(W["v3_b64_l4096"], B=5, H=16, lengths=(1, 127, 128, 129, 4096),
+                                       seed=2111),
+        # the largest multi-token decode the boundary takes (T = 8), 8 x 16 = 128 rows
+        "t8_h16": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, T=8, H=16, lengths=(8, 300), seed=2112),
     }
 
 
@@ -128,7 +134,8 @@ def test_end_to_end_vs_normal_path(mk, name):
 
 @pytest.mark.parametrize("part", ["f32", "bf16"])
 @pytest.mark.parametrize("S", [2, 3, 7])
-@pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64", "mtp_p16_tail"])
+@pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64", "mtp_p16_tail", "history_matrix",
+                                  "t8_h16"])
 def test_split_partials_and_merge(mk, name, S, part):
     import torch
     log(f"[split] {name} S={S} partials={part}")
