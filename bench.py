@@ -207,6 +207,23 @@ def main():
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1e3 / K
 
+    # cache append of the step's new rows (written at position L - T + t of each
+    # sequence; the timed cache's own rows there are overwritten, which changes
+    # no timing)
+    c_new = torch.randn((B, T, 512), device=dev).to(torch.bfloat16)
+    kpe_new = torch.randn((B, T, 64), device=dev).to(torch.bfloat16)
+    app_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+    for i in range(args.warmup):
+        mk.mla_append_cache(c_new, kpe_new, kv[i % R], block_table, seqlens)
+    for i in range(K):
+        app_evs[i][0].record(stream)
+        mk.mla_append_cache(c_new, kpe_new, kv[i % R], block_table, seqlens)
+        app_evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    app_ms = float(np.mean([a.elapsed_time(b) for a, b in app_evs]))
+    app_bytes = 2 * B * T * (512 + 64) * 2 + 4 * B * 2   # rows read + written, seqlens, table entries
+
     if args.copy_calibration:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
         # factor that turns those counters into bytes for the decode kernel
@@ -264,6 +281,9 @@ def main():
             "chain_eager_ms_per_step": eager_ms_per_step,
             "chain_alg_bytes": chain_algorithmic(case, dec_bytes),
             "chain_TBps": chain_algorithmic(case, dec_bytes) / (ms_per_step * 1e-3) / 1e12,
+            "append_us": app_ms * 1e3,
+            "append_alg_bytes": app_bytes,
+            "append_GBps": app_bytes / (app_ms * 1e-3) / 1e9,
         },
     }
     if not args.no_cpu:

@@ -20,6 +20,9 @@
  *   mla_unabsorb_out   out = W_UV latent                ("MLA in full detail", Step 4:
  *                                                       fold W_UV into the output)
  *
+ * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
+ * written at their paged positions before the decode that reads them).
+ *
  * "M5.8" is the page "M5.8 - Multi-Head Latent Attention: Latent KV State,
  * Weight Absorption, and FlashMLA"; "mlxcel" is its "MLA absorbed decode" page.
  *
@@ -162,6 +165,32 @@ int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* pa
  * (einsum bhqc,hvc->bhqv; W_UV [H,d_V,d_c]). */
 int mla_unabsorb_out(const void* latent, mla_dtype latent_dtype, const uint16_t* w_uv, float* out,
                      int B, int T, int H, int r, int d_V, void* stream);
+
+/* Cache append: writes the T new rows [c (r) || k_pe (d_R)] of every sequence
+ * into the paged cache, new row t of sequence b at logical position
+ * j = seqlens[b] - T + t, i.e. at physical row
+ *     block_table[b, j / page_size] * page_size + j % page_size
+ * -- the convention mla_decode_latent reads with (seqlens counts the T new
+ * rows).  Bytes are copied unchanged.  Rows whose position or block-table
+ * entry is out of range are skipped (mla_validate_inputs checks the table).
+ *   c_new [B,T,r] bf16, kpe_new [B,T,d_R] bf16 (already rotated),
+ *   kv_cache [num_blocks,page_size,r+d_R] bf16 (written), block_table
+ *   [B,max_blocks_per_seq] int32, seqlens [B] int32 (lengths after the append)
+ * All pointers are device memory owned by the caller; c_new, kpe_new and
+ * kv_cache 16-byte aligned, the int32 arrays 4-byte aligned.  Errors (nothing
+ * is launched): MLA_ERR_SHAPE for B, num_blocks or max_blocks_per_seq < 0,
+ * T < 1, or (B > 0) num_blocks or max_blocks_per_seq == 0;
+ * MLA_ERR_UNSUPPORTED for r != 512, d_R != 64, T > 8, page_size not a
+ * multiple of 16 in [16, 1024], or B*T > 2^24; MLA_ERR_NULL / MLA_ERR_ALIGN
+ * for pointers.  B == 0 is a no-op.
+ * Source: M5.8 0x05, "Prefill publication contract" and "Exact phase
+ * algorithms and commit state" (the decode step takes the new row once, at the
+ * position the page table assigns it) and "Paged and ragged address
+ * translation".  Synchronisation: stream order; the decode that reads the rows
+ * must be launched after this call on the same stream (or after an event). */
+int mla_append_cache(const uint16_t* c_new, const uint16_t* kpe_new, uint16_t* kv_cache, int num_blocks,
+                     int page_size, const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seqlens, int B, int T, int r, int d_R, void* stream);
 
 /* Synchronous check of the device-resident index data of mla_decode_latent:
  * every needed block-table entry is in [0, num_blocks) and every seqlen is in

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
 * ``mla_decode_latent`` latent attention over the paged cache ("MLA in full detail", Step 3)
 * ``mla_merge_splits``  log-sum-exp merge of split partials   (M5.8 0x0C)
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
+* ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
 * ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
 
 ``absorbed_decode`` chains the four calls for one decode step.
@@ -57,9 +58,10 @@ def load_library():
                                     P, SZ, P, I, P, P, P, I, P, P]
     L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
-                 "mla_merge_splits", "mla_unabsorb_out", "mla_validate_inputs"):
+                 "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_validate_inputs"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -203,6 +205,20 @@ def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
     return out
 
 
+def mla_append_cache(c_new, kpe_new, kv_cache, block_table, seqlens, stream=None):
+    """Write the T new rows of every sequence at positions seqlens[b]-T+t of the
+    paged cache (in place).  c_new [B,T,512] bf16, kpe_new [B,T,64] bf16."""
+    B, T, r = c_new.shape
+    dr = kpe_new.shape[2]
+    num_blocks, page_size, _ = kv_cache.shape
+    if tuple(kpe_new.shape[:2]) != (B, T) or seqlens.shape[0] < B or block_table.shape[0] < B:
+        raise ValueError("mla_append_cache: c_new, kpe_new, seqlens and block_table disagree on B, T")
+    _check(load_library().mla_append_cache(_ptr(c_new), _ptr(kpe_new), _ptr(kv_cache), num_blocks, page_size,
+                                           _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, T, r,
+                                           dr, _stream(stream)), "mla_append_cache")
+    return kv_cache
+
+
 def mla_validate_inputs(block_table, seqlens, T, max_seqlen, page_size, num_blocks, stream=None):
     """Synchronous index check; returns the status code (0 = valid)."""
     B = seqlens.shape[0]
@@ -234,5 +250,6 @@ def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, ma
 __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_merge_splits",
-    "mla_unabsorb_out", "mla_validate_inputs", "DecodeBuffers", "softmax_scale", "absorbed_decode",
+    "mla_unabsorb_out", "mla_append_cache", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
+    "absorbed_decode",
 ]

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_latent.so")
-SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip"]
+SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -229,6 +229,26 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   return MLA_OK;
 }
 
+int mla_append_cache(const uint16_t* c_new, const uint16_t* kpe_new, uint16_t* kv_cache, int num_blocks,
+                     int page_size, const int32_t* block_table, int max_blocks_per_seq,
+                     const int32_t* seqlens, int B, int T, int r, int d_R, void* stream) {
+  if (B < 0 || num_blocks < 0 || max_blocks_per_seq < 0) return MLA_ERR_SHAPE;
+  if (T < 1) return MLA_ERR_SHAPE;
+  if (T > kMaxT) return MLA_ERR_UNSUPPORTED;
+  if (r != kR || d_R != kDR) return MLA_ERR_UNSUPPORTED;
+  if (page_size < 16 || page_size > 1024 || page_size % 16) return MLA_ERR_UNSUPPORTED;
+  if (B == 0) return MLA_OK;
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return MLA_ERR_SHAPE;
+  int st;
+  if ((st = check_ptr16(c_new)) || (st = check_ptr16(kpe_new)) || (st = check_ptr16(kv_cache)) ||
+      (st = check_ptr4(block_table)) || (st = check_ptr4(seqlens)))
+    return st;
+  if ((long long)B * T > (1LL << 24)) return MLA_ERR_UNSUPPORTED;  // grid of B*T/4 workgroups
+  mla::AppendParams p{c_new, kpe_new, kv_cache, block_table, seqlens, B, T, page_size, max_blocks_per_seq,
+                      num_blocks};
+  return launch_status(mla::launch_append(p, (hipStream_t)stream));
+}
+
 int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* part_lse,
                      const int32_t* split_indptr, int B, int T, int H, int r, void* out_latent,
                      mla_dtype out_dtype, float* lse, void* stream) {

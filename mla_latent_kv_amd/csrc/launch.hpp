@@ -58,11 +58,21 @@ struct UnabsorbParams {
   int M, H;
 };
 
+struct AppendParams {
+  const uint16_t* c_new;       // [B,T,512] bf16
+  const uint16_t* kpe_new;     // [B,T,64] bf16
+  uint16_t* cache;             // [num_blocks,P,576] bf16
+  const int32_t* block_table;  // [B,max_blocks]
+  const int32_t* seqlens;      // [B], counting the T new rows
+  int B, T, page_size, max_blocks, num_blocks;
+};
+
 // max_units: upper bound of work items x n_rg (the grid is derived from it)
 hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st);
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipStream_t st);
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);
 hipError_t launch_unabsorb(const UnabsorbParams& p, bool latent_f32, hipStream_t st);
+hipError_t launch_append(const AppendParams& p, hipStream_t st);
 
 }  // namespace mla

@@ -100,6 +100,31 @@ def phys_row(block_table, b, j, page_size, num_blocks) -> int:
     return int(lib().mlao_phys_row(_p(bt), bt.shape[1], b, j, page_size, num_blocks))
 
 
+def append_rows(kv_cache, block_table, seqlens, c_new, kpe_new, page_size):
+    """Cache append of a decode step (M5.8 0x05, "Exact phase algorithms and
+    commit state": the step's new row is stored once, at its own position;
+    "Paged and ragged address translation" for where that row lives).
+
+    ``seqlens`` are the lengths after the step, so new row t of sequence b is
+    logical position seqlens[b] - T + t.  Returns a new cache array with those
+    rows set to [c_new || kpe_new] (bit patterns copied); rows whose position
+    has no mapped page are skipped."""
+    out = np.array(kv_cache, dtype=np.uint16, copy=True)
+    flat = out.reshape(-1, out.shape[-1])
+    B, T, r = c_new.shape
+    for b in range(B):
+        for t in range(T):
+            j = int(seqlens[b]) - T + t
+            if j < 0:
+                continue
+            row = phys_row(block_table, b, j, page_size, out.shape[0])
+            if row < 0:
+                continue
+            flat[row, :r] = c_new[b, t]
+            flat[row, r:] = kpe_new[b, t]
+    return out
+
+
 def dims(case):
     """(d_nope, d_rope, d_v, r) read off the array shapes of a case."""
     return (case.q_nope.shape[-1], case.q_pe.shape[-1], case.w_uv.shape[1], case.w_uk.shape[2])

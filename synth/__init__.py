@@ -238,3 +238,44 @@ def normal_f32(shape, seed, std=1.0) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(seed))
     x = rng.standard_normal(size=shape, dtype=np.float32)
     return x * np.float32(std) if std != 1.0 else x
+
+
+@dataclasses.dataclass
+class Growth:
+    """Inputs of a multi-step decode: ``base`` holds the cache before the first
+    step (lengths ``base.seqlens``), with pages already mapped up to the
+    lengths after the last step and every row at or past the current length
+    poisoned; ``steps[s]`` holds that step's new cache rows and queries."""
+    base: Case
+    final_seqlens: np.ndarray
+    steps: list   # dicts: c_new [B,T,r], kpe_new [B,T,d_R], q_lat [B,T,H,r], q_pe [B,T,H,d_R]
+
+
+def make_growth(wl: Workload, n_steps: int, poison: bool = True) -> Growth:
+    """``wl``'s lengths are those after ``n_steps`` decode steps of T tokens
+    each; the sequences start ``n_steps * T`` rows shorter.  The new rows and
+    per-step positional queries are N(0, 1) bf16 draws, the absorbed queries
+    N(0, 1/4) (the spread of W_UK^T q_nope under the recipe: 128 terms of
+    variance 1/512), from a second generator seeded from ``wl.seed`` (the
+    base case uses the first, as in ``make_case``)."""
+    case = make_case(wl, poison=poison)
+    B, T, H, P = wl.B, wl.T, wl.H, wl.page_size
+    grow = n_steps * T
+    final = case.seqlens.copy()
+    start = final - grow
+    if (start < 0).any():
+        raise ValueError("every sequence must hold the rows the steps append")
+    if poison:
+        for b in range(B):
+            for j in range(int(start[b]), int(final[b])):
+                page, off = divmod(j, P)
+                case.kv_cache[case.block_table[b, page], off, :] = BF16_NAN
+    case.seqlens = start.astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 0x5EED))
+    steps = []
+    for _ in range(n_steps):
+        steps.append(dict(c_new=_normal_bf16(rng, (B, T, wl.r)),
+                          kpe_new=_normal_bf16(rng, (B, T, wl.d_rope)),
+                          q_lat=_normal_bf16(rng, (B, T, H, wl.r), 0.5),
+                          q_pe=_normal_bf16(rng, (B, T, H, wl.d_rope))))
+    return Growth(case, final.astype(np.int32), steps)

@@ -134,6 +134,30 @@ def test_merge_validation(lib):
 
 
 def test_binding_names_match_abi():
-    for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out",
+    for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
         assert callable(getattr(mk, n))
+
+
+def _append(lib, **kw):
+    a = dict(c=P16, k=P16, kv=P16, nb=64, P=64, bt=P16, mb=64, sl=P16, B=2, T=1, r=512, dr=64)
+    a.update(kw)
+    return lib.mla_append_cache(a["c"], a["k"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"], a["sl"],
+                                a["B"], a["T"], a["r"], a["dr"], None)
+
+
+def test_append_validation(lib):
+    assert _append(lib, r=256) == UNSUP
+    assert _append(lib, dr=32) == UNSUP
+    assert _append(lib, P=24) == UNSUP
+    assert _append(lib, P=2048) == UNSUP
+    assert _append(lib, T=9) == UNSUP
+    assert _append(lib, T=0) == SHAPE
+    assert _append(lib, B=-1) == SHAPE
+    assert _append(lib, nb=0) == SHAPE
+    assert _append(lib, mb=0) == SHAPE
+    assert _append(lib, c=None) == NULL
+    assert _append(lib, kv=P17) == ALIGN
+    assert _append(lib, bt=ctypes.c_void_p((1 << 20) + 2)) == ALIGN
+    assert _append(lib, B=1 << 22, T=8) == UNSUP     # more rows than one launch covers
+    assert _append(lib, B=0, c=None, k=None, kv=None, bt=None, sl=None) == OK

@@ -14,6 +14,7 @@ What pins what:
 * negative controls: the mistakes M5.8 0x04 and mlxcel Stage 2 name must fail
   the product tolerance.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -413,3 +414,100 @@ def test_log2_lse_units_fail():
     assert not _fails(good, lat)
     wrong, _ = oracle.merge(po, pl * math.log2(math.e), plan[0])
     assert _fails(wrong, lat)
+
+
+# --------------------------------------------------------------------------
+# 7. cache append of a decode step (M5.8 0x05)
+
+def _chunked_rebuild(case, T, shift=0):
+    """Start from an all-NaN pool with the case's block table and append the
+    case's logical rows T at a time (``shift`` offsets the lengths passed)."""
+    rows = oracle.gather_rows(case)     # logical rows through divmod, not phys_row
+    pool = np.full_like(case.kv_cache, synth.BF16_NAN)
+    L = case.seqlens.astype(np.int64)
+    r = case.kv_cache.shape[-1] - case.q_pe.shape[-1]
+    for s in range(int(math.ceil(L.max() / T))):
+        cur = np.minimum(T * (s + 1), L)   # a finished sequence re-appends its last rows
+        c_new = np.empty((case.B, T, r), np.uint16)
+        k_new = np.empty((case.B, T, case.kv_cache.shape[-1] - r), np.uint16)
+        for b in range(case.B):
+            lb = rows[b]
+            for t in range(T):
+                j = int(cur[b]) - T + t
+                v = synth.f32_to_bf16_bits(lb[max(j, 0)].astype(np.float32))
+                c_new[b, t], k_new[b, t] = v[:r], v[r:]
+        pool = oracle.append_rows(pool, case.block_table, (cur + shift).astype(np.int32),
+                                  c_new, k_new, case.page_size)
+    return pool
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_append_rebuilds_the_paged_cache(T):
+    """Appending every sequence's rows in steps of T tokens, each at
+    seqlens - T + t, reproduces the paged pool bit for bit (poisoned tails and
+    unused blocks stay NaN): the append position agrees with the read-side
+    address formula."""
+    case = tiny(301, B=3, H=2, lengths=(36, 21, 9), P=8, unused=0.2)
+    assert np.array_equal(_chunked_rebuild(case, T), case.kv_cache)
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_append_off_by_one_position_fails(shift):
+    """Negative control: lengths that exclude (or double count) the new rows
+    put them one position off, which the rebuild detects."""
+    case = tiny(302, B=3, H=2, lengths=(36, 21, 9), P=8)
+    assert not np.array_equal(_chunked_rebuild(case, 3, shift), case.kv_cache)
+
+
+def test_append_skips_unmapped_positions():
+    bt = np.array([[1, -1]], np.int32)
+    pool = np.zeros((2, 4, 6), np.uint16)
+    c = np.full((1, 2, 4), 7, np.uint16)
+    k = np.full((1, 2, 2), 9, np.uint16)
+    out = oracle.append_rows(pool, bt, np.array([5], np.int32), c, k, 4)
+    # positions 3 (block 1, offset 3) and 4 (page 1 unmapped: skipped)
+    assert (out[1, 3] == [7, 7, 7, 7, 9, 9]).all()
+    out[1, 3] = 0
+    assert not out.any()
+
+
+def _explicit_latent(ql, qp, rows, T, scale):
+    """numpy latent attention over explicit logical rows (causal over T)."""
+    r = ql.shape[-1]
+    c, kpe = rows[:, :r], rows[:, r:]
+    n = rows.shape[0]
+    s = (np.einsum("thc,jc->thj", ql, c) + np.einsum("thd,jd->thj", qp, kpe)) * scale
+    for t in range(T):
+        s[t, :, n - T + t + 1:] = -np.inf
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    return np.einsum("thj,jc->thc", p, c)
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_multistep_decode_sees_the_appended_rows(T):
+    """Three decode steps: after each append the oracle's paged latent
+    attention equals attention over the explicit concatenation of the
+    starting rows and every row appended so far."""
+    wl = synth.Workload("grow", B=3, T=T, H=2, L=0, page_size=8, seed=303,
+                        lengths=(19, 8 + 3 * T, 3 * T), r=16, d_rope=4, d_nope=8, d_v=6)
+    g = synth.make_growth(wl, 3)
+    case = g.base
+    start = oracle.gather_rows(case)
+    cache = case.kv_cache
+    scale = 1.0 / math.sqrt(8 + 4)
+    for s, st in enumerate(g.steps):
+        lens = (g.base.seqlens + (s + 1) * T).astype(np.int32)
+        cache = oracle.append_rows(cache, case.block_table, lens, st["c_new"], st["kpe_new"],
+                                   case.page_size)
+        cs = dataclasses.replace(case, kv_cache=cache, seqlens=lens, q_pe=st["q_pe"])
+        ql = oracle.bf16_to_f64(st["q_lat"])
+        lat, _ = oracle.latent_attention(cs, ql, scale=scale)
+        for b in range(wl.B):
+            new = [np.concatenate([oracle.bf16_to_f64(g.steps[k]["c_new"][b]),
+                                   oracle.bf16_to_f64(g.steps[k]["kpe_new"][b])], -1)
+                   for k in range(s + 1)]
+            rows = np.concatenate([start[b]] + new, 0)
+            ref = _explicit_latent(ql[b], oracle.bf16_to_f64(st["q_pe"][b]), rows, T, scale)
+            assert np.allclose(lat[b], ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(g.final_seqlens, g.base.seqlens + 3 * T)
