@@ -213,6 +213,40 @@ def latent_attention(case, q_lat, scale=None, plan=None, pairs=None, nthreads=No
     return lat, lse
 
 
+def sparse_latent_attention(q_lat, q_pe, kv_cache, indices, topk_length, scale):
+    """Sparse absorbed decode in fp64 (M5.8 0x0B, "Sparse indices are physical
+    execution metadata"; 0x08, sparse mode of the runtime ABI).
+
+    Query row (b, t, h) attends, without a causal mask, to the cache rows
+    ``indices[b, t, k]`` -- flat physical row ids page * P + offset, read with
+    no block table -- for k < min(topk_length[b], topk) (every k when
+    ``topk_length`` is None), with the score of the dense path,
+    (q~ . c + q_pe . k_pe) * scale.  A repeated id counts once per occurrence.
+    Returns (latent [B,T,H,r], lse [B,T,H]); a row with no valid entry gives
+    latent 0 and lse -inf."""
+    ql = _c(q_lat, np.float64)
+    qp = bf16_to_f64(q_pe)
+    B, T, H, r = ql.shape
+    rows = kv_cache.reshape(-1, kv_cache.shape[-1])
+    topk = indices.shape[2]
+    lat = np.zeros((B, T, H, r))
+    lse = np.full((B, T, H), -np.inf)
+    for b in range(B):
+        n = topk if topk_length is None else max(0, min(int(topk_length[b]), topk))
+        if n == 0:
+            continue
+        for t in range(T):
+            sel = bf16_to_f64(rows[np.asarray(indices[b, t, :n], dtype=np.int64)])
+            c, kpe = sel[:, :r], sel[:, r:]
+            s = (ql[b, t] @ c.T + qp[b, t] @ kpe.T) * scale      # [H, n]
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            z = e.sum(axis=1, keepdims=True)
+            lat[b, t] = (e @ c) / z
+            lse[b, t] = (m + np.log(z))[:, 0]
+    return lat, lse
+
+
 def merge(part_out, part_lse, split_indptr):
     """Exact LSE merge of normalised partials (M5.8 0x0C); returns (latent, lse)."""
     po = _c(part_out, np.float64)

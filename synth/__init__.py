@@ -279,3 +279,116 @@ def make_growth(wl: Workload, n_steps: int, poison: bool = True) -> Growth:
                           q_lat=_normal_bf16(rng, (B, T, H, wl.r), 0.5),
                           q_pe=_normal_bf16(rng, (B, T, H, wl.d_rope))))
     return Growth(case, final.astype(np.int32), steps)
+
+
+@dataclasses.dataclass
+class SparseCase:
+    """Inputs of a sparse (top-k) decode: each query token (b, t) attends to the
+    cache rows listed in ``indices[b, t, :]`` -- physical row ids
+    page * P + offset -- of which the first ``topk_length[b]`` are valid."""
+    wl: Workload
+    q_lat: np.ndarray         # [B,T,H,r] uint16 (absorbed query, bf16 bits)
+    q_pe: np.ndarray          # [B,T,H,d_R] uint16
+    kv_cache: np.ndarray      # [num_blocks,P,r+d_R] uint16
+    indices: np.ndarray       # [B,T,topk] int32
+    topk_length: Optional[np.ndarray]  # [B] int32, or None (all topk valid)
+    seqlens: np.ndarray       # [B] context lengths the positions were drawn from
+    block_table: np.ndarray   # [B,max_blocks] (layout record; the sparse path reads no table)
+
+    @property
+    def B(self): return self.wl.B
+
+    @property
+    def T(self): return self.wl.T
+
+    @property
+    def H(self): return self.wl.H
+
+    @property
+    def topk(self): return self.indices.shape[2]
+
+    @property
+    def page_size(self): return self.wl.page_size
+
+    @property
+    def num_blocks(self): return self.kv_cache.shape[0]
+
+
+def make_sparse(wl: Workload, topk: int, valid: Optional[tuple] = None, poison: bool = True,
+                junk: bool = True, duplicates: bool = False, use_length: bool = True) -> SparseCase:
+    """Draw a sparse decode workload (fixed draw order, ``Generator(PCG64(wl.seed))``):
+
+    1. context lengths L_b as in ``make_case`` (explicit, ragged or ``wl.L``);
+    2. q_lat [B,T,H,r] ~ N(0, 1/4) (the spread of W_UK^T q_nope under the recipe),
+       q_pe [B,T,H,d_R] ~ N(0, 1);
+    3. the paged layout: pages of each sequence at a seeded permutation of the
+       physical blocks (as in ``make_case``);
+    4. per query token (b, t): n_b = min(topk, L_b) distinct positions drawn
+       uniformly without replacement from [0, L_b), in draw order, stored as
+       physical rows block_table[b, j // P] * P + j % P (``duplicates`` then
+       overwrites every fourth entry with the entry before it);
+    5. the valid prefix: ``valid[b]`` when given, else n_b; entries past it are
+       junk (-1 and 2^31 - 1 alternately) when ``junk`` is set, else repeat the
+       last valid entry;
+    6. the values of every selected row ~ N(0, 1); all other rows bf16 NaN
+       (``poison``) or zero.
+
+    ``use_length`` False passes no topk_length (every entry valid; then
+    ``valid`` must be None and every L_b >= topk)."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    B, T, H, P = wl.B, wl.T, wl.H, wl.page_size
+    if wl.lengths is not None:
+        seqlens = np.asarray(wl.lengths, dtype=np.int32)
+    elif wl.ragged is not None:
+        lo, hi = wl.ragged
+        u = rng.uniform(math.log(lo), math.log(hi), size=B)
+        seqlens = np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+    else:
+        seqlens = np.full(B, wl.L, dtype=np.int32)
+    r, dr = wl.r, wl.d_rope
+    q_lat = _normal_bf16(rng, (B, T, H, r), 0.5)
+    q_pe = _normal_bf16(rng, (B, T, H, dr))
+    pages = [max((int(L) + P - 1) // P, 1) for L in seqlens]
+    n_phys = sum(pages)
+    perm = rng.permutation(n_phys).astype(np.int32) if wl.permute else np.arange(n_phys, dtype=np.int32)
+    block_table = np.full((B, max(pages)), -1, dtype=np.int32)
+    k = 0
+    for b in range(B):
+        for p in range(pages[b]):
+            block_table[b, p] = perm[k]
+            k += 1
+    nb = np.minimum(topk, seqlens).astype(np.int32)
+    if valid is not None:
+        nv = np.asarray(valid, dtype=np.int32)
+        if nv.shape != (B,) or (nv > nb).any() or (nv < 0).any():
+            raise ValueError("valid prefix lengths must lie in [0, min(topk, L_b)]")
+    else:
+        nv = nb
+    if not use_length and (valid is not None or (nb < topk).any()):
+        raise ValueError("without topk_length every entry must be valid")
+    indices = np.empty((B, T, topk), dtype=np.int32)
+    for b in range(B):
+        for t in range(T):
+            pos = rng.choice(int(seqlens[b]), size=int(nb[b]), replace=False)
+            phys = block_table[b, pos // P].astype(np.int64) * P + pos % P
+            row = np.empty(topk, dtype=np.int64)
+            row[:nb[b]] = phys
+            if duplicates:
+                for i in range(3, int(nv[b]), 4):
+                    row[i] = row[i - 1]
+            n = int(nv[b])
+            if junk:
+                row[n:] = np.where(np.arange(topk - n) % 2 == 0, -1, 2 ** 31 - 1)
+            elif n > 0:
+                row[n:] = row[n - 1]
+            else:
+                row[:] = 0
+            indices[b, t] = row.astype(np.int32)
+    fill = BF16_NAN if poison else np.uint16(0)
+    kv_cache = np.full((n_phys, P, r + dr), fill, dtype=np.uint16)
+    sel = np.unique(np.concatenate([indices[b, t, :nv[b]] for b in range(B) for t in range(T)]
+                                   + [np.empty(0, np.int32)]).astype(np.int64))
+    flat = kv_cache.reshape(-1, r + dr)
+    flat[sel] = _normal_bf16(rng, (sel.shape[0], r + dr))
+    return SparseCase(wl, q_lat, q_pe, kv_cache, indices, nv.astype(np.int32) if use_length else None,
+                      seqlens, block_table)

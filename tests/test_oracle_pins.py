@@ -511,3 +511,110 @@ def test_multistep_decode_sees_the_appended_rows(T):
             ref = _explicit_latent(ql[b], oracle.bf16_to_f64(st["q_pe"][b]), rows, T, scale)
             assert np.allclose(lat[b], ref, rtol=1e-12, atol=1e-12)
     assert np.array_equal(g.final_seqlens, g.base.seqlens + 3 * T)
+
+
+# --------------------------------------------------------------------------
+# 8. sparse (top-k) decode (M5.8 0x0B)
+
+def _sparse_tiny(seed, T=1, lengths=(40, 9), topk=12, **kw):
+    wl = synth.Workload("sp", B=len(lengths), T=T, H=3, L=0, page_size=8, seed=seed,
+                        lengths=lengths, r=16, d_rope=4, d_nope=8, d_v=6)
+    return synth.make_sparse(wl, topk, **kw)
+
+
+def _sparse(sc, scale=0.3, indices=None, lengths="case"):
+    return oracle.sparse_latent_attention(oracle.bf16_to_f64(sc.q_lat), sc.q_pe, sc.kv_cache,
+                                          sc.indices if indices is None else indices,
+                                          sc.topk_length if lengths == "case" else lengths, scale)
+
+
+def test_sparse_full_selection_equals_dense():
+    """Selecting every position of the sequence, as physical rows through the
+    block table, is dense decode: the sparse oracle (numpy) agrees with the
+    dense one (the C oracle) for T = 1."""
+    case = tiny(401, B=3, T=1, H=3, lengths=(37, 8, 20), P=8)
+    ql = synth.normal_bf16((3, 1, 3, 16), 402, std=0.5)
+    topk = 40
+    idx = np.full((3, 1, topk), -1, np.int32)
+    for b in range(3):
+        for j in range(int(case.seqlens[b])):
+            idx[b, 0, j] = oracle.phys_row(case.block_table, b, j, case.page_size, case.num_blocks)
+    scale = 1.0 / math.sqrt(8 + 4)
+    got, got_lse = oracle.sparse_latent_attention(oracle.bf16_to_f64(ql), case.q_pe, case.kv_cache, idx,
+                                                  case.seqlens, scale)
+    ref, ref_lse = oracle.latent_attention(case, oracle.bf16_to_f64(ql), scale=scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(got_lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_order_of_selection_is_irrelevant():
+    sc = _sparse_tiny(403, T=2)
+    lat, lse = _sparse(sc)
+    idx = sc.indices.copy()
+    rng = np.random.default_rng(5)
+    for b in range(sc.B):
+        for t in range(sc.T):
+            n = int(sc.topk_length[b])
+            idx[b, t, :n] = rng.permutation(idx[b, t, :n])
+    lat2, lse2 = _sparse(sc, indices=idx)
+    assert np.allclose(lat, lat2, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, lse2, rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_entries_past_the_valid_prefix_are_ignored():
+    sc = _sparse_tiny(404, T=2, valid=(5, 9))
+    lat, lse = _sparse(sc)
+    idx = sc.indices.copy()
+    idx[0, :, 5:] = 3
+    idx[1, :, 9:] = 0
+    lat2, lse2 = _sparse(sc, indices=idx)
+    assert np.array_equal(lat, lat2) and np.array_equal(lse, lse2)
+
+
+def test_sparse_single_key_and_empty_selection():
+    """One valid entry: the latent is that row's c and lse its score; no valid
+    entry: latent 0 and lse -inf."""
+    sc = _sparse_tiny(405, valid=(1, 0))
+    lat, lse = _sparse(sc)
+    row = oracle.bf16_to_f64(sc.kv_cache.reshape(-1, 20)[sc.indices[0, 0, 0]])
+    ql = oracle.bf16_to_f64(sc.q_lat[0, 0])
+    qp = oracle.bf16_to_f64(sc.q_pe[0, 0])
+    for h in range(sc.H):
+        assert np.allclose(lat[0, 0, h], row[:16], rtol=0, atol=0)
+        assert math.isclose(lse[0, 0, h], 0.3 * (ql[h] @ row[:16] + qp[h] @ row[16:]), rel_tol=1e-12)
+    assert (lat[1] == 0).all() and np.isneginf(lse[1]).all()
+
+
+def test_sparse_repeated_entry_counts_twice():
+    """Selecting rows (a, a, b): softmax weights 2 e^{s_a} and e^{s_b}."""
+    sc = _sparse_tiny(406, lengths=(40,), topk=3, use_length=False)
+    idx = sc.indices.copy()
+    idx[0, 0, 1] = idx[0, 0, 0]
+    lat, lse = _sparse(sc, indices=idx, lengths=None)
+    rows = oracle.bf16_to_f64(sc.kv_cache.reshape(-1, 20)[idx[0, 0, [0, 2]].astype(np.int64)])
+    ql = oracle.bf16_to_f64(sc.q_lat[0, 0])
+    qp = oracle.bf16_to_f64(sc.q_pe[0, 0])
+    for h in range(sc.H):
+        sa, sb = (0.3 * (ql[h] @ rows[i, :16] + qp[h] @ rows[i, 16:]) for i in range(2))
+        wa, wb = 2 * math.exp(sa), math.exp(sb)
+        want = (wa * rows[0, :16] + wb * rows[1, :16]) / (wa + wb)
+        assert np.allclose(lat[0, 0, h], want, rtol=1e-12, atol=1e-13)
+        assert math.isclose(lse[0, 0, h], math.log(wa + wb), rel_tol=1e-12)
+
+
+def test_sparse_logical_ids_negative_control():
+    """M5.8 0x0B: the entries are physical rows.  Reading them as logical token
+    positions (through the block table) attends to other rows and fails the
+    product tolerance."""
+    sc = _sparse_tiny(407, T=2, lengths=(40, 33), topk=12)
+    lat, _ = _sparse(sc)
+    P = sc.page_size
+    wrong = sc.indices.copy()
+    for b in range(sc.B):
+        for t in range(sc.T):
+            for k in range(int(sc.topk_length[b])):
+                j = int(sc.indices[b, t, k])
+                if j < int(sc.seqlens[b]):
+                    wrong[b, t, k] = sc.block_table[b, j // P] * P + j % P
+    bad, _ = _sparse(sc, indices=wrong)
+    assert _fails(bad, lat)
