@@ -14,6 +14,9 @@ K eager steps bracket the decode kernel with HIP events on the launch stream to
 get its own duration, from which the roofline fraction is computed; the chain
 throughput (`value`) then comes from K replays of the step captured as a HIP
 graph (one graph per replica; `--no-graph` times the eager launches instead).
+The sparse (top-k) decode kernel is timed the same way on its own workload
+(64 x 2048 selected rows of 32768-token contexts) and reported under
+``detail`` (``--no-sparse`` skips it).
 
 Prints one JSON line (rank 0, one GPU).
 """
@@ -59,6 +62,94 @@ def chain_algorithmic(case, decode_bytes):
     return decode_bytes + absorb + unabsorb
 
 
+def sparse_algorithmic(sc, n_splits):
+    """Algorithmic bytes and FLOPs of one sparse decode launch (split partials in
+    bf16): every valid selected row once, its index entry, the query, the
+    partial outputs and their lse."""
+    import numpy as np
+    B, T, H = sc.B, sc.T, sc.H
+    n = sc.topk if sc.topk_length is None else np.minimum(sc.topk_length, sc.topk).astype(np.int64)
+    keys = int(np.sum(n)) * T if sc.topk_length is not None else B * T * sc.topk
+    q_bytes = B * T * H * (512 + 64) * 2
+    out_bytes = B * T * n_splits * H * (512 * 2 + 4)
+    nbytes = keys * (ROW_BYTES + 4) + q_bytes + out_bytes
+    flops = 2 * H * keys * (576 + 512)
+    return nbytes, flops
+
+
+def bench_sparse(name, K, W, R, dev):
+    """Time the sparse (top-k) decode kernel on its workload: HIP events around
+    each launch on its stream, cache replicas rotating."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    sc = synth.make_sparse(synth.SPARSE_WORKLOADS[name], synth.SPARSE_TOPK[name], poison=False)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv0 = bf16(sc.kv_cache)
+    kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    q_lat, q_pe = bf16(sc.q_lat), bf16(sc.q_pe)
+    idx = torch.from_numpy(sc.indices).to(dev)
+    tl = torch.from_numpy(sc.topk_length).to(dev)
+    buf = mk.SparseBuffers(sc.B, sc.T, sc.H, sc.topk, 0, dev, part_dtype=torch.bfloat16)
+    S = buf.num_splits
+    lat = torch.empty((sc.B, sc.T, sc.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((sc.B, sc.T, sc.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    scale = mk.softmax_scale()
+    BT = sc.B * sc.T
+
+    def run(r, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mk.mla_decode_sparse(q_lat, q_pe, kv[r], idx, tl, scale, buffers=buf, merge=False)
+        if ev is not None:
+            ev[1].record(stream)
+        if S > 1:
+            mk.mla_merge_splits(buf.part_out.view(BT * S, 1, sc.H, 512), buf.part_lse.view(BT * S, 1, sc.H),
+                                buf.split_indptr, BT, out_latent=lat.view(BT, 1, sc.H, 512),
+                                lse=lse.view(BT, 1, sc.H))
+
+    for i in range(W):
+        run(i % R)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        run(i % R, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes, flops = sparse_algorithmic(sc, S)
+    del kv, kv0
+    torch.cuda.empty_cache()
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "decode_sparse_hbm_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            from mla_latent_kv_amd import _build
+            rec = json.load(open(tpath))
+            if rec.get("source_sha256") == _build.kernel_source_hash() and rec.get("workload") == name \
+                    and int(rec.get("splits", -1)) == S:
+                traffic = rec["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    return {
+        "sparse_workload": name, "sparse_topk": sc.topk, "sparse_context": int(sc.seqlens.max()),
+        "sparse_splits": S,
+        "sparse_decode_us": us,
+        "sparse_step_us": (t1 - t0) * 1e6 / K,
+        "sparse_alg_bytes": nbytes,
+        "sparse_GBps": nbytes / (us * 1e-6) / 1e9,
+        "sparse_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "sparse_tflops": flops / (us * 1e-6) / 1e12,
+        "sparse_traffic": traffic,
+    }
+
+
 def cpu_baseline(case, pairs_n, threads, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys)."""
@@ -101,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the chain with eager launches instead of replaying a captured HIP graph")
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the sparse (top-k) decode measurement reported under detail")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -286,6 +379,8 @@ def main():
             "append_GBps": app_bytes / (app_ms * 1e-3) / 1e9,
         },
     }
+    if not args.no_sparse:
+        result["detail"].update(bench_sparse("v3_sparse_b64_topk2048", K, args.warmup, R, dev))
     if not args.no_cpu:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))

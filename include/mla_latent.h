@@ -21,7 +21,8 @@
  *                                                       fold W_UV into the output)
  *
  * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
- * written at their paged positions before the decode that reads them).
+ * written at their paged positions before the decode that reads them); for
+ * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent.
  *
  * "M5.8" is the page "M5.8 - Multi-Head Latent Attention: Latent KV State,
  * Weight Absorption, and FlashMLA"; "mlxcel" is its "MLA absorbed decode" page.
@@ -143,6 +144,42 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       void* workspace, size_t workspace_bytes, void* part_out,
                       mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
                       void* out_latent, mla_dtype out_dtype, float* lse, void* stream);
+
+/* Split count of mla_decode_sparse: num_splits > 0 is returned as is; 0 picks
+ * S = clamp(floor(CUs / (B*T*ceil(H/128))), 1, ceil(topk/256)) (and at most
+ * 128), enough work units for every CU with chunks of at least 256 entries.
+ * The split partial buffers of mla_decode_sparse hold B*T*S rows. */
+int mla_sparse_split_count(int B, int T, int H, int topk, int num_splits, int* splits);
+
+/* Sparse (top-k) absorbed latent attention.  Query token (b, t) -- all H heads
+ * -- attends to the cache rows listed in its index row, without a causal mask:
+ *   indices     [B,T,topk] int32: physical row ids page * page_size + offset of
+ *               the pool (no block table is read); entries past the valid
+ *               prefix are never used (any value).  A repeated id counts once
+ *               per occurrence.  Ids outside [0, num_blocks*page_size) inside
+ *               the valid prefix are undefined behaviour (clamped into the
+ *               pool, so never read outside it).
+ *   topk_length [B] int32, nullable: valid prefix of the index rows of sequence
+ *               b (clamped to [0, topk]); NULL means all topk entries.  A row
+ *               with no valid entry gives out_latent 0 and lse -inf.
+ *   q_lat, q_pe, kv_cache, softmax_scale, out_latent, out_dtype, lse: as for
+ *               mla_decode_latent (kv_cache of at most 2^32 - 1 rows).
+ *   num_splits  S from mla_sparse_split_count (0 = automatic): with S > 1 the
+ *               valid prefix of every index row is cut into S chunks of
+ *               ceil(ceil(n/S)/32)*32 entries; partial rows follow the
+ *               mla_decode_latent layout over the B*T query tokens
+ *               (part_out [B*T*S,H,r], part_lse [B*T*S,H], split_indptr
+ *               [B*T+1]; merge over B*T "sequences" of one token each).
+ * Source: M5.8 0x0B "Sparse indices are physical execution metadata" (the
+ * index layout, physical ids, valid-prefix lengths) and 0x08 (sparse mode of
+ * the runtime ABI: no causal mask).  The score, softmax and value sum are
+ * those of mla_decode_latent over the selected rows. */
+int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                      int num_blocks, int page_size, const int32_t* indices, int topk,
+                      const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                      float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                      float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                      float* lse, void* stream);
 
 /* Merge of split partial states, per (b,t,h) over rows k in
  * [split_indptr[b], split_indptr[b+1]):  M = max_k lse_k, w_k = exp(lse_k - M),

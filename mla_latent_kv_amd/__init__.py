@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
 * ``mla_merge_splits``  log-sum-exp merge of split partials   (M5.8 0x0C)
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
 * ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
+* ``mla_decode_sparse``  top-k latent attention over physical row ids (M5.8 0x0B)
 * ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
 
 ``absorbed_decode`` chains the four calls for one decode step.
@@ -59,9 +60,12 @@ def load_library():
     L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
+    L.mla_sparse_split_count.argtypes = [I, I, I, I, I, P]
+    L.mla_decode_sparse.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, F, I, P, I, P, P, P, I, P, P]
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
-                 "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_validate_inputs"):
+                 "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
+                 "mla_decode_sparse", "mla_validate_inputs"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -219,6 +223,64 @@ def mla_append_cache(c_new, kpe_new, kv_cache, block_table, seqlens, stream=None
     return kv_cache
 
 
+def mla_sparse_split_count(B, T, H, topk, num_splits=0) -> int:
+    """Split count mla_decode_sparse uses (0 = automatic)."""
+    sc = ctypes.c_int(0)
+    _check(load_library().mla_sparse_split_count(B, T, H, topk, num_splits, ctypes.byref(sc)),
+           "mla_sparse_split_count")
+    return int(sc.value)
+
+
+class SparseBuffers:
+    """Caller-owned split partials of mla_decode_sparse (B*T*S rows)."""
+
+    def __init__(self, B, T, H, topk, num_splits, device, part_dtype=None):
+        torch = _torch()
+        self.num_splits = mla_sparse_split_count(B, T, H, topk, num_splits)
+        self.part_out = self.part_lse = self.split_indptr = None
+        if self.num_splits > 1:
+            n = max(B * T * self.num_splits, 1)
+            self.part_out = torch.empty((n, H, R_LATENT), dtype=part_dtype or torch.float32, device=device)
+            self.part_lse = torch.empty((n, H), dtype=torch.float32, device=device)
+            self.split_indptr = torch.empty(B * T + 1, dtype=torch.int32, device=device)
+
+
+def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale, num_splits=0,
+                      out_dtype=None, buffers: Optional[SparseBuffers] = None, out_latent=None, lse=None,
+                      merge=True, stream=None):
+    """Sparse (top-k) latent attention (see include/mla_latent.h).
+
+    indices [B,T,topk] int32 physical rows, topk_length [B] int32 or None.
+    Returns (out_latent, lse); with more than one split and merge=False the
+    partials stay in ``buffers`` and (None, None) is returned."""
+    torch = _torch()
+    B, T, H, r = q_lat.shape
+    dr = q_pe.shape[3]
+    num_blocks, page_size, _ = kv_cache.shape
+    topk = indices.shape[2]
+    if tuple(indices.shape[:2]) != (B, T) or (topk_length is not None and topk_length.shape[0] < B):
+        raise ValueError("mla_decode_sparse: indices / topk_length do not match q_lat")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if buffers is None:
+        buffers = SparseBuffers(B, T, H, topk, num_splits, q_lat.device)
+    S = buffers.num_splits
+    want_out = S == 1 or merge
+    if want_out and out_latent is None:
+        out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
+    if want_out and lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q_lat.device)
+    split = S != 1
+    _check(load_library().mla_decode_sparse(
+        _ptr(q_lat), _ptr(q_pe), _ptr(kv_cache), num_blocks, page_size, _ptr(indices), topk,
+        _ptr(topk_length), B, T, H, r, dr, float(softmax_scale), S,
+        _ptr(buffers.part_out if split else None),
+        _dtype_code(buffers.part_out.dtype) if split else MLA_F32,
+        _ptr(buffers.part_lse if split else None), _ptr(buffers.split_indptr if split else None),
+        _ptr(out_latent if want_out else None), _dtype_code(out_dtype),
+        _ptr(lse if want_out else None), _stream(stream)), "mla_decode_sparse")
+    return (out_latent, lse) if want_out else (None, None)
+
+
 def mla_validate_inputs(block_table, seqlens, T, max_seqlen, page_size, num_blocks, stream=None):
     """Synchronous index check; returns the status code (0 = valid)."""
     B = seqlens.shape[0]
@@ -250,6 +312,7 @@ def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, ma
 __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_merge_splits",
-    "mla_unabsorb_out", "mla_append_cache", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
+    "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
+    "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",
 ]

@@ -229,6 +229,100 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   return MLA_OK;
 }
 
+int mla_sparse_split_count(int B, int T, int H, int topk, int num_splits, int* splits) {
+  if (!splits) return MLA_ERR_NULL;
+  if (B < 0 || topk < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  int st = check_heads(T, H);
+  if (st) return st;
+  if (num_splits > 0) {
+    *splits = num_splits;
+    return MLA_OK;
+  }
+  if (B == 0) {
+    *splits = 1;
+    return MLA_OK;
+  }
+  // every index row has the same capacity topk: one uniform split count that
+  // brings the work units up to the CU count, with chunks of at least
+  // kMinChunk entries
+  int cus = 0;
+  if ((st = device_cus(&cus))) return st;
+  const long long units = (long long)B * T * ((H + 127) / 128);
+  long long sc = cus / units;
+  sc = std::min<long long>(sc, (topk + kMinChunk - 1) / kMinChunk);
+  sc = std::min<long long>(std::max<long long>(sc, 1), kAutoCap);
+  *splits = (int)sc;
+  return MLA_OK;
+}
+
+int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                      int num_blocks, int page_size, const int32_t* indices, int topk,
+                      const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                      float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                      float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                      float* lse, void* stream) {
+  if (B < 0 || num_blocks < 1 || topk < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  int st = check_heads(T, H);
+  if (st) return st;
+  if (r != kR || d_R != kDR) return MLA_ERR_UNSUPPORTED;
+  if (page_size < 16 || page_size > 1024 || page_size % 16) return MLA_ERR_UNSUPPORTED;
+  if (out_dtype != MLA_BF16 && out_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (part_dtype != MLA_BF16 && part_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  const long long rows = (long long)num_blocks * page_size;
+  if (rows > 0xFFFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_ptr16(q_lat)) || (st = check_ptr16(q_pe)) || (st = check_ptr16(kv_cache))) return st;
+  if ((st = check_ptr4(indices))) return st;
+  if ((topk_length && !aligned4(topk_length)) || (lse && !aligned4(lse))) return MLA_ERR_ALIGN;
+  int S = 0;
+  if ((st = mla_sparse_split_count(B, T, H, topk, num_splits, &S))) return st;
+
+  // the kernel's work sequences are the B*T query tokens, one query row group
+  // per token (its H heads), each over its own index row
+  const long long BT = (long long)B * T;
+  const int n_rg = (H + 127) / 128;
+  if (BT * S * n_rg > (1LL << 31) - 8) return MLA_ERR_SHAPE;
+  mla::DecodeParams p{};
+  p.q_lat = q_lat;
+  p.q_pe = q_pe;
+  p.cache = kv_cache;
+  p.indices = indices;
+  p.topk_length = topk_length;
+  p.topk = topk;
+  p.sp_T = T;
+  p.num_rows = (uint32_t)rows;
+  p.B = (int)BT;
+  p.T = 1;
+  p.H = H;
+  p.page_size = 32;  // chunk rounding of the uniform split: whole 32-entry steps
+  p.n_rg = n_rg;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  if (S == 1) {
+    if ((st = check_ptr16(out_latent))) return st;
+    p.out = out_latent;
+    p.lse = lse;
+    p.n_units = (int)(BT * n_rg);
+    return launch_status(mla::launch_decode(p, p.n_units, false, out_dtype == MLA_F32, s, true));
+  }
+  if (!part_out || !part_lse || !split_indptr) return MLA_ERR_WORKSPACE;
+  if (!aligned16(part_out) || !aligned4(part_lse) || !aligned4(split_indptr)) return MLA_ERR_ALIGN;
+  if (out_latent && !aligned16(out_latent)) return MLA_ERR_ALIGN;
+  p.part_out = part_out;
+  p.part_lse = part_lse;
+  p.split_indptr = split_indptr;
+  p.num_splits = S;
+  p.n_units = (int)(BT * S * n_rg);
+  const bool part_f32 = part_dtype == MLA_F32;
+  if ((st = launch_status(mla::launch_decode(p, p.n_units, true, part_f32, s, true)))) return st;
+  if (out_latent) {
+    mla::MergeParams mp{part_out, part_lse, split_indptr, (int)BT, H, out_latent, lse};
+    return launch_status(mla::launch_merge(mp, part_f32, out_dtype == MLA_F32, s));
+  }
+  return MLA_OK;
+}
+
 int mla_append_cache(const uint16_t* c_new, const uint16_t* kpe_new, uint16_t* kv_cache, int num_blocks,
                      int page_size, const int32_t* block_table, int max_blocks_per_seq,
                      const int32_t* seqlens, int B, int T, int r, int d_R, void* stream) {

@@ -88,6 +88,24 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t
                : "memory");
 }
 
+// 16 bytes per lane from a 64-bit per-lane address into LDS at lds_addr + 16 * lane.
+// The immediate offset OFF moves the global address and the LDS destination
+// alike, so M0 is set to lds_addr - OFF (one address register serves all the
+// 128-byte column steps of a row).
+template <int OFF>
+__device__ __forceinline__ void dma16v(const void* addr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(addr),
+               "s"(lds_addr - OFF), "n"(OFF)
+               : "memory");
+}
+
+// 4 bytes per lane (scalar base + vector offset) into LDS at lds_addr + 4 * lane.
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds_addr)
+               : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

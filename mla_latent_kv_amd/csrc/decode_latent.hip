@@ -160,6 +160,9 @@ constexpr Slot slot_of(int s) {
 }
 // softmax stages of the next step, by slot
 constexpr int kSmLoad = 45, kSmCheck = 46, kSmRef = 47, kSmExp0 = 48, kSmSum = 64, kSmPack = 65;
+// sparse mode: slot at which the row ids of a later step are read back (after
+// the last load instruction of the step)
+constexpr int kSpIds = 57;
 // value MFMA v: token block kb = v >> 4 (16 tokens), row block ri = (v >> 2) & 3
 // (the rows of wave w + ri), this wave's column block cb = v & 3
 
@@ -170,8 +173,22 @@ constexpr int dma_part_at(int s) {
              ? (s - kDmaSlot0) / kDmaStride
              : -1;
 }
+static_assert(kDmaSlot0 + 8 * kDmaStride < kSpIds && kSpIds < kSmPack,
+              "sparse ids are read after the step's last load and before the probability writes");
 
-template <int NB, bool SPLIT, bool OUT_F32>
+// Key count of work sequence bb: its length, or in sparse mode the valid
+// prefix of its index row (sequence bb / sp_T's topk_length, at most topk).
+template <bool SPARSE>
+__device__ __forceinline__ int unit_keys(const DecodeParams& p, int bb) {
+  if constexpr (SPARSE) {
+    if (!p.topk_length) return p.topk;
+    return min(max(p.topk_length[bb / p.sp_T], 0), p.topk);
+  } else {
+    return p.seqlens[bb];
+  }
+}
+
+template <int NB, bool SPLIT, bool OUT_F32, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // step ring; after the last step it is reused to stage the 128 KB output block
   constexpr int kRingBytes = NB * kStepBytes > 128 * 1024 ? NB * kStepBytes : 128 * 1024;
@@ -207,7 +224,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       const int S = p.num_splits;
       b = item / S;
       const int s = item - b * S;
-      const int Lb = p.seqlens[b];
+      const int Lb = unit_keys<SPARSE>(p, b);
       const int chunk = (((Lb + S - 1) / S + p.page_size - 1) / p.page_size) * p.page_size;
       j0 = min(s * chunk, Lb);
       j1 = min(j0 + chunk, Lb);
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   } else {
     b = item;
     j0 = 0;
-    j1 = p.seqlens[b];
+    j1 = unit_keys<SPARSE>(p, b);
     slot = b;
   }
   // work-unit scalars are wave-uniform: keep them in scalar registers
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   j0 = __builtin_amdgcn_readfirstlane(j0);
   j1 = __builtin_amdgcn_readfirstlane(j1);
   slot = __builtin_amdgcn_readfirstlane(slot);
-  const int L = __builtin_amdgcn_readfirstlane(p.seqlens[b]);
+  const int L = __builtin_amdgcn_readfirstlane(unit_keys<SPARSE>(p, b));
   const int T = p.T, H = p.H, TH = T * H;
   const int P = p.page_size;
   const int row0 = rg * kRowsPerWG;
@@ -266,6 +283,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // lane; the page of the next half-tile is tracked incrementally.
   const int hw = w >> 1;
   const uint32_t dma_voff = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4) + 64 * (w & 1);
+  const int rsw = (l & 15) ^ tile_swz(l >> 4);  // sparse: row of the half this lane loads
+  const uint32_t dma_coff = 16 * (l >> 4) + 64 * (w & 1);
   int pg_base = 0, pg_vec = 0;
   auto load_window = [&](int base) {
     pg_base = base;
@@ -295,8 +314,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     dma_page = jt / P;
     dma_off = jt - dma_page * P;
   };
-  dma_reset();
-  load_window(dma_page);
+  // Sparse mode: no pages.  The row of every lane comes from the unit's index
+  // row (entry j0 + 32 it + 16 hw + rsw for step it, clamped into the list and
+  // the row id into the pool).  The first NB steps' ids are loaded here; each
+  // later step's 32 ids arrive by a direct-to-LDS load issued NB steps ahead
+  // into this wave's quarter of the idle probability buffer (see the step body).
+  const int32_t* const idx_row = SPARSE ? p.indices + (size_t)b * p.topk : nullptr;
+  auto idx_of = [&](int it) { return min(j0 + kStepTok * it + 16 * hw + rsw, p.topk - 1); };
+  int sidx_pro[NB];
+  int sidx = 0;  // row id of this lane for the next step to issue
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int it = 0; it < NB; ++it) sidx_pro[it] = idx_row[idx_of(it)];
+  } else {
+    dma_reset();
+    load_window(dma_page);
+  }
   // The query rows are loaded after the page ids, so the compiler's wait for the
   // page ids (at their first use) leaves the query loads in flight, overlapped
   // with the first tile loads.  The score MFMAs of the first step consume all of
@@ -308,12 +341,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   for (int ks = 0; ks < kDR / 16; ++ks) q[kR / 16 + ks] = *(const bf16x8*)(qp + 16 * ks);
   // consume the page ids here: the compiler's wait for them then counts the
   // query loads behind them exactly
-  asm volatile("" ::"v"(pg_vec));
+  if constexpr (SPARSE) {
+#pragma unroll
+    for (int it = 0; it < NB; ++it) asm volatile("" ::"v"(sidx_pro[it]));
+  } else {
+    asm volatile("" ::"v"(pg_vec));
+  }
   auto dma_start = [&]() {
     if (half_live(0)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRowBytes;
   };
 
   const uint8_t* dma_base = cache;
+  const uint8_t* dma_vaddr = cache;  // sparse: this lane's row + dma_coff
   uint32_t dma_dst = 0;
   // A half past the end of the range (the second half of a short last step,
   // and every load issued past the last step: the pipeline issues NB-1 steps
@@ -322,8 +361,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // reads a buffer filled past the last step.  This keeps the issue path and
   // the wait counts free of branches.
   auto issue_prep = [&](int it) {
-    dma_base = half_live(it) ? dma_row : cache;
     dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
+    if constexpr (SPARSE) {
+      const uint32_t row = half_live(it) ? min((uint32_t)sidx, p.num_rows - 1u) : (uint32_t)rsw;
+      dma_vaddr = cache + (uint64_t)row * kRowBytes + dma_coff;
+      return;
+    }
+    dma_base = half_live(it) ? dma_row : cache;
     // advance to the same half of the next step
     dma_off += kStepTok;
     if (dma_off >= P) {
@@ -340,7 +384,22 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   };
   auto issue_part = [&](auto n_const) {
     constexpr int n = decltype(n_const)::value;
-    dma16s(dma_voff + 128 * n, dma_base, dma_dst + 2048 * n);
+    if constexpr (SPARSE) dma16v<128 * n>(dma_vaddr, dma_dst + 2048 * n);
+    else dma16s(dma_voff + 128 * n, dma_base, dma_dst + 2048 * n);
+  };
+  // sparse: during step i, the ids of step i + NB (entries j0 + 32 (i + NB) +
+  // (l & 31)) go to this wave's quarter of probability buffer (i + 1) & 1,
+  // which no wave touches between the barrier of step i and this wave's own
+  // probability writes for step i + 1 (slot kSmPack); the ids are read back at
+  // slot kSpIds, after a wait for the load
+  // probability buffer: [step parity][token block][row block][lane] x 16 B
+  constexpr uint32_t kPbufRowBlock = 64 * 16, kPbufParity = 2 * 4 * kPbufRowBlock;
+  static_assert(2 * kPbufParity == sizeof(pbuf), "probability buffer layout");
+  const uint32_t ids_lds0 = lds_addr_of(pbuf) + w * kPbufRowBlock;  // token block 0, row block w
+  auto ids_lds = [&](int i) { return ids_lds0 + ((i + 1) & 1) * kPbufParity; };
+  auto idx_dma = [&](int i) {
+    const uint32_t voff = 4u * (uint32_t)min(j0 + kStepTok * (i + NB) + (l & 31), p.topk - 1);
+    dma4s(voff, idx_row, ids_lds(i));
   };
   auto issue = [&](int it) {
     issue_prep(it);
@@ -534,17 +593,31 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
   if (nsteps > 0) for (int pass = 0;; ++pass) {
     if (pass > 0) {
-      dma_reset();
-      load_window(dma_page);
+      if constexpr (SPARSE) {
+#pragma unroll
+        for (int it = 0; it < NB; ++it) sidx_pro[it] = idx_row[idx_of(it)];
+      } else {
+        dma_reset();
+        load_window(dma_page);
+      }
       __builtin_amdgcn_s_waitcnt(0);
     }
-    dma_start();
+    if constexpr (!SPARSE) dma_start();
     if (pass > 0) {
       l_part = 0.f;
 #pragma unroll
       for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
     }
-    for (int it = 0; it < NB - 1; ++it) issue(it);
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int it = 0; it < NB - 1; ++it) {
+        sidx = sidx_pro[it];
+        issue(it);
+      }
+      sidx = sidx_pro[NB - 1];
+    } else {
+      for (int it = 0; it < NB - 1; ++it) issue(it);
+    }
 
     // One-stage pipeline.  Step i (after its barrier): value MFMAs of step i
     // (probabilities pv from the softmax at the end of step i-1) interleaved
@@ -576,6 +649,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     // body of step i (this wave's loads of step i+NB-1 are issued in it)
     auto step = [&](int i) {
       issue_prep(i + NB - 1);
+      if constexpr (SPARSE) idx_dma(i);
       const bool full = j0 + kStepTok * (i + 2) <= lim_lo;  // step i+1 needs no mask
       // K of step i+1 (after the last step: a resident stale buffer, whose
       // scores the mask discards)
@@ -614,6 +688,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           }
         }
         if constexpr (dma_part_at(s) >= 0) issue_part(std::integral_constant<int, dma_part_at(s)>{});
+        if constexpr (SPARSE && s == kSpIds) {
+          // the ids of step i + NB have landed once at most the nine tile loads
+          // issued after them are in flight
+          wait_vm<9>();
+          sidx = *(const __attribute__((address_space(3))) int*)(uintptr_t)(ids_lds(i) + 4 * (16 * hw + rsw));
+        }
         // softmax of step i+1 (past the last step every score is masked)
         if constexpr (s == kSmLoad) {
           sm_load(Sn);
@@ -875,22 +955,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
   }
 }
 
-template <int NB, bool SPLIT, bool F32>
+template <int NB, bool SPLIT, bool F32, bool SPARSE>
 static hipError_t launch_decode_t(const DecodeParams& prm, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<NB, SPLIT, F32>), dim3(grid), dim3(256), 0, st, prm);
+  hipLaunchKernelGGL((decode_kernel<NB, SPLIT, F32, SPARSE>), dim3(grid), dim3(256), 0, st, prm);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& prm, int max_units, bool split, bool out_f32,
-                         hipStream_t st) {
+                         hipStream_t st, bool sparse) {
   constexpr int NB = 4;
   const int grid = ((max_units + 7) / 8) * 8;  // whole XCD rounds; extra workgroups exit
-  if (split) {
-    if (out_f32) return launch_decode_t<NB, true, true>(prm, grid, st);
-    return launch_decode_t<NB, true, false>(prm, grid, st);
+  if (sparse) {
+    if (split) {
+      if (out_f32) return launch_decode_t<NB, true, true, true>(prm, grid, st);
+      return launch_decode_t<NB, true, false, true>(prm, grid, st);
+    }
+    if (out_f32) return launch_decode_t<NB, false, true, true>(prm, grid, st);
+    return launch_decode_t<NB, false, false, true>(prm, grid, st);
   }
-  if (out_f32) return launch_decode_t<NB, false, true>(prm, grid, st);
-  return launch_decode_t<NB, false, false>(prm, grid, st);
+  if (split) {
+    if (out_f32) return launch_decode_t<NB, true, true, false>(prm, grid, st);
+    return launch_decode_t<NB, true, false, false>(prm, grid, st);
+  }
+  if (out_f32) return launch_decode_t<NB, false, true, false>(prm, grid, st);
+  return launch_decode_t<NB, false, false, false>(prm, grid, st);
 }
 
 hipError_t launch_plan(const PlanParams& prm, hipStream_t st) {

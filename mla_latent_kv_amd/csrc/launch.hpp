@@ -24,6 +24,12 @@ struct DecodeParams {
   float* part_lse;             // split mode: [*,T,H] f32
   void* out;                   // unsplit: [B,T,H,512] bf16 or f32
   float* lse;                  // unsplit: [B,T,H] f32, nullable
+  // sparse (top-k) mode: the kernel's "sequences" are the B*T query tokens
+  // (T = 1 above); each reads the rows listed in its index row
+  const int32_t* indices;      // [B*T, topk] physical row ids
+  const int32_t* topk_length;  // [B] valid prefix per sequence, nullable
+  int topk, sp_T;              // entries per index row; query tokens per sequence
+  uint32_t num_rows;           // rows in the cache pool (index clamp)
 };
 
 struct PlanParams {
@@ -68,7 +74,8 @@ struct AppendParams {
 };
 
 // max_units: upper bound of work items x n_rg (the grid is derived from it)
-hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st,
+                         bool sparse = false);
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipStream_t st);
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);

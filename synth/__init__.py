@@ -281,6 +281,17 @@ def make_growth(wl: Workload, n_steps: int, poison: bool = True) -> Growth:
     return Growth(case, final.astype(np.int32), steps)
 
 
+# Sparse decode workload: the headline geometry (B = 64, H = 128, page 64) over
+# 32768-token contexts with 2048 rows selected per query token (top-k over
+# physical rows, M5.8 0x0B).  The pages give no top-k value; 2048 of 32768 is
+# one sixteenth of the context.
+SPARSE_WORKLOADS = {
+    "v3_sparse_b64_topk2048": Workload("v3_sparse_b64_topk2048", B=64, T=1, H=128, L=32768, page_size=64,
+                                       seed=1006),
+}
+SPARSE_TOPK = {"v3_sparse_b64_topk2048": 2048}
+
+
 @dataclasses.dataclass
 class SparseCase:
     """Inputs of a sparse (top-k) decode: each query token (b, t) attends to the

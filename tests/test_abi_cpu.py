@@ -135,6 +135,7 @@ def test_merge_validation(lib):
 
 def test_binding_names_match_abi():
     for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache",
+              "mla_decode_sparse", "mla_sparse_split_count",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
         assert callable(getattr(mk, n))
 
@@ -161,3 +162,43 @@ def test_append_validation(lib):
     assert _append(lib, bt=ctypes.c_void_p((1 << 20) + 2)) == ALIGN
     assert _append(lib, B=1 << 22, T=8) == UNSUP     # more rows than one launch covers
     assert _append(lib, B=0, c=None, k=None, kv=None, bt=None, sl=None) == OK
+
+
+def _sparse(lib, **kw):
+    a = dict(q=P16, qp=P16, kv=P16, nb=64, P=64, idx=P16, topk=2048, tl=None, B=2, T=1, H=128, r=512,
+             dr=64, scale=0.07, S=1, po=None, pdt=1, pl=None, si=None, out=P16, odt=0, lse=None)
+    a.update(kw)
+    return lib.mla_decode_sparse(a["q"], a["qp"], a["kv"], a["nb"], a["P"], a["idx"], a["topk"], a["tl"],
+                                 a["B"], a["T"], a["H"], a["r"], a["dr"], ctypes.c_float(a["scale"]),
+                                 a["S"], a["po"], a["pdt"], a["pl"], a["si"], a["out"], a["odt"], a["lse"],
+                                 None)
+
+
+def test_sparse_validation(lib):
+    assert _sparse(lib, r=256) == UNSUP
+    assert _sparse(lib, dr=32) == UNSUP
+    assert _sparse(lib, T=9) == UNSUP
+    assert _sparse(lib, H=129) == UNSUP
+    assert _sparse(lib, P=24) == UNSUP
+    assert _sparse(lib, odt=4) == UNSUP
+    assert _sparse(lib, topk=0) == SHAPE
+    assert _sparse(lib, nb=0) == SHAPE
+    assert _sparse(lib, S=-1) == SHAPE
+    assert _sparse(lib, scale=-1.0) == SHAPE
+    assert _sparse(lib, nb=1 << 23, P=1024) == UNSUP      # more than 2^32 - 1 rows
+    assert _sparse(lib, q=None) == NULL
+    assert _sparse(lib, idx=None) == NULL
+    assert _sparse(lib, idx=ctypes.c_void_p((1 << 20) + 2)) == ALIGN
+    assert _sparse(lib, tl=ctypes.c_void_p((1 << 20) + 2)) == ALIGN
+    assert _sparse(lib, out=None) == NULL                  # one split needs out_latent
+    assert _sparse(lib, S=4) == WS                         # split without partial buffers
+    assert _sparse(lib, S=4, po=P17, pl=P16, si=P16) == ALIGN
+    assert _sparse(lib, B=0, q=None, out=None, idx=None) == OK
+
+
+def test_sparse_split_count(lib):
+    sc = ctypes.c_int(0)
+    assert lib.mla_sparse_split_count(64, 1, 128, 2048, 4, ctypes.byref(sc)) == OK and sc.value == 4
+    assert lib.mla_sparse_split_count(0, 1, 128, 2048, 0, ctypes.byref(sc)) == OK and sc.value == 1
+    assert lib.mla_sparse_split_count(64, 1, 128, 0, 0, ctypes.byref(sc)) == SHAPE
+    assert lib.mla_sparse_split_count(64, 1, 128, 16, 0, None) == NULL
