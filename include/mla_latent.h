@@ -45,7 +45,9 @@
  *
  * Fixed geometry of this build: kv_lora_rank r = 512, rope width d_R = 64,
  * d_nope = d_V = 128.  H (query heads) is 1..128, T (query tokens per
- * sequence) is 1..8, page_size is a multiple of 16 in [16, 1024].
+ * sequence: 1 for plain decode, a few for multi-token decode, up to a
+ * prefill-sized block when comparing with the Normal path) is 1..1024,
+ * page_size is a multiple of 16 in [16, 1024].
  */
 #ifndef MLA_LATENT_H
 #define MLA_LATENT_H
@@ -181,6 +183,38 @@ int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
                       float* lse, void* stream);
 
+/* Workspace of mla_decode_normal: the chunk's gathered latent and rope rows,
+ * its up-projected keys and values ([B*chunk,H,128] bf16 each) and, with more
+ * than one chunk (ceil(max_seqlen/chunk) > 1), the running state carried
+ * between chunks.  B*chunk is at most 2^24. */
+int mla_normal_workspace_size(int B, int T, int H, int max_seqlen, int chunk, size_t* workspace_bytes);
+
+/* The Normal (non-absorbed) path on the GPU, for comparison with the absorbed
+ * one: every cached latent is up-projected per head, k_nope = W_UK[h] c_j and
+ * v_j = W_UV[h] c_j, and each head attends with the 192-wide key
+ * [k_nope || k_pe] and the 128-wide value -- the same function as mla_absorb_q
+ * + mla_decode_latent + mla_unabsorb_out, computed in the other association
+ * order ("MLA in full detail", Steps 2-3 before the weights are folded; M5.8
+ * 0x05 naive path).  The cache is processed `chunk` tokens per sequence at a
+ * time (the chunked-KV form: rows gathered through the block table, two
+ * rocBLAS GEMMs for the up-projection, an MFMA attention kernel that carries
+ * the running max, sum and unnormalised output from chunk to chunk: the exact
+ * log-sum-exp combination of M5.8 0x0C).
+ *   q_nope [B,T,H,128], q_pe [B,T,H,64], w_uk, w_uv [H,128,512] bf16; cache,
+ *   block_table, seqlens, max_seqlen, softmax_scale as for mla_decode_latent
+ *   (causal over the T current rows).
+ *   out [B,T,H,128] f32, lse [B,T,H] f32 (nullable).
+ * rocBLAS keeps one handle per device (created on the first call, held until
+ * the process ends, with rocBLAS's own workspace); this is the one entry point
+ * that allocates.  Returns MLA_ERR_WORKSPACE when the workspace is missing or
+ * smaller than mla_normal_workspace_size reports. */
+int mla_decode_normal(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk,
+                      const uint16_t* w_uv, const uint16_t* kv_cache, int num_blocks, int page_size,
+                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens, int B,
+                      int T, int H, int d_nope, int d_R, int d_V, int r, int max_seqlen,
+                      float softmax_scale, int chunk, void* workspace, size_t workspace_bytes, float* out,
+                      float* lse, void* stream);
+
 /* Merge of split partial states, per (b,t,h) over rows k in
  * [split_indptr[b], split_indptr[b+1]):  M = max_k lse_k, w_k = exp(lse_k - M),
  * lse = M + log(sum_k w_k), out = sum_k w_k * part_out[k] / sum_k w_k.  Rows with
@@ -217,7 +251,7 @@ int mla_unabsorb_out(const void* latent, mla_dtype latent_dtype, const uint16_t*
  * kv_cache 16-byte aligned, the int32 arrays 4-byte aligned.  Errors (nothing
  * is launched): MLA_ERR_SHAPE for B, num_blocks or max_blocks_per_seq < 0,
  * T < 1, or (B > 0) num_blocks or max_blocks_per_seq == 0;
- * MLA_ERR_UNSUPPORTED for r != 512, d_R != 64, T > 8, page_size not a
+ * MLA_ERR_UNSUPPORTED for r != 512, d_R != 64, T > 1024, page_size not a
  * multiple of 16 in [16, 1024], or B*T > 2^24; MLA_ERR_NULL / MLA_ERR_ALIGN
  * for pointers.  B == 0 is a no-op.
  * Source: M5.8 0x05, "Prefill publication contract" and "Exact phase

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
 * ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
 * ``mla_decode_sparse``  top-k latent attention over physical row ids (M5.8 0x0B)
+* ``mla_decode_normal``  the Normal path on the GPU (per-head K/V), for comparison
 * ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
 
 ``absorbed_decode`` chains the four calls for one decode step.
@@ -61,11 +62,15 @@ def load_library():
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
     L.mla_sparse_split_count.argtypes = [I, I, I, I, I, P]
+    L.mla_normal_workspace_size.argtypes = [I, I, I, I, I, P]
+    L.mla_decode_normal.argtypes = [P, P, P, P, P, I, I, P, I, P, I, I, I, I, I, I, I, I, F, I, P,
+                                     ctypes.c_size_t, P, P, P]
     L.mla_decode_sparse.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, F, I, P, I, P, P, P, I, P, P]
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
-                 "mla_decode_sparse", "mla_validate_inputs"):
+                 "mla_decode_sparse", "mla_normal_workspace_size", "mla_decode_normal",
+                 "mla_validate_inputs"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -281,6 +286,40 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     return (out_latent, lse) if want_out else (None, None)
 
 
+def mla_normal_workspace_size(B, T, H, max_seqlen, chunk) -> int:
+    nb = ctypes.c_size_t(0)
+    _check(load_library().mla_normal_workspace_size(B, T, H, max_seqlen, chunk, ctypes.byref(nb)),
+           "mla_normal_workspace_size")
+    return int(nb.value)
+
+
+def mla_decode_normal(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                      chunk=None, workspace=None, out=None, lse=None, stream=None):
+    """Normal-path decode on the GPU (up-projected per-head K/V, chunked).
+
+    Returns (out [B,T,H,128] f32, lse [B,T,H] f32).  ``chunk`` defaults to
+    max_seqlen (one chunk)."""
+    torch = _torch()
+    B, T, H, dn = q_nope.shape
+    dr = q_pe.shape[3]
+    dv, r = w_uv.shape[1], w_uk.shape[2]
+    num_blocks, page_size, _ = kv_cache.shape
+    chunk = int(max_seqlen) if chunk is None else int(chunk)
+    need = mla_normal_workspace_size(B, T, H, int(max_seqlen), chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_nope.device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q_nope.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q_nope.device)
+    _check(load_library().mla_decode_normal(
+        _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), _ptr(kv_cache), num_blocks, page_size,
+        _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, T, H, dn, dr, dv, r, int(max_seqlen),
+        float(softmax_scale), chunk, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+        _stream(stream)), "mla_decode_normal")
+    return out, lse
+
+
 def mla_validate_inputs(block_table, seqlens, T, max_seqlen, page_size, num_blocks, stream=None):
     """Synchronous index check; returns the status code (0 = valid)."""
     B = seqlens.shape[0]
@@ -313,6 +352,6 @@ __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_merge_splits",
     "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
-    "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
+    "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",
 ]

@@ -10,7 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_latent.so")
-SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip"]
+SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip", "normal.hip"]
+# the Normal path's up-projection GEMMs are rocBLAS calls
+LINK_LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -54,7 +56,7 @@ def build(verbose: bool = False) -> str:
     if errors:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
     tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LINK_LIBS]
     subprocess.check_call(link)
     os.replace(tmp, LIB)
     return LIB

@@ -73,6 +73,25 @@ struct AppendParams {
   int B, T, page_size, max_blocks, num_blocks;
 };
 
+struct NormalParams {
+  const uint16_t* q_nope;      // [B,T,H,128]
+  const uint16_t* q_pe;        // [B,T,H,64]
+  const uint16_t* cache;       // [num_blocks,P,576]
+  const int32_t* block_table;  // [B,max_blocks]
+  const int32_t* seqlens;      // [B]
+  uint16_t* lat;               // [B*chunk,512] gathered latent rows of the chunk
+  uint16_t* rope;              // [B*chunk,64]  their rope parts
+  const uint16_t* kbuf;        // [B*chunk,H,128] up-projected keys
+  const uint16_t* vbuf;        // [B*chunk,H,128] up-projected values
+  float* o_state;              // [B,T,H,128] unnormalised output carried between chunks
+  float* m_state;              // [B,T,H] running max (log2 units)
+  float* l_state;              // [B,T,H] running sum
+  float* out;                  // [B,T,H,128]
+  float* lse;                  // [B,T,H], nullable
+  int B, T, H, page_size, max_blocks, chunk, c, first, last;
+  float scale_log2;
+};
+
 // max_units: upper bound of work items x n_rg (the grid is derived from it)
 hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st,
                          bool sparse = false);
@@ -81,5 +100,7 @@ hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipSt
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);
 hipError_t launch_unabsorb(const UnabsorbParams& p, bool latent_f32, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, hipStream_t st);
+hipError_t launch_gather(const NormalParams& p, hipStream_t st);
+hipError_t launch_mha(const NormalParams& p, hipStream_t st);
 
 }  // namespace mla

@@ -51,7 +51,7 @@ def test_absorb_validation(lib):
     f = lib.mla_absorb_q
     assert f(P16, P16, P16, 2, 1, 128, 64, 512, None) == UNSUP     # d_nope != 128
     assert f(P16, P16, P16, 2, 1, 128, 128, 256, None) == UNSUP    # r != 512
-    assert f(P16, P16, P16, 2, 9, 128, 128, 512, None) == UNSUP    # T > 8
+    assert f(P16, P16, P16, 2, 1025, 128, 128, 512, None) == UNSUP  # T > 1024
     assert f(P16, P16, P16, 2, 1, 129, 128, 512, None) == UNSUP    # H > 128
     assert f(P16, P16, P16, 2, 0, 128, 128, 512, None) == SHAPE    # T < 1
     assert f(P16, P16, P16, -1, 1, 128, 128, 512, None) == SHAPE
@@ -85,7 +85,7 @@ def test_decode_validation(lib):
     assert _decode(lib, dr=32) == UNSUP
     assert _decode(lib, P=24) == UNSUP          # not a multiple of 16
     assert _decode(lib, P=2048) == UNSUP
-    assert _decode(lib, T=9) == UNSUP
+    assert _decode(lib, T=1025) == UNSUP
     assert _decode(lib, odt=5) == UNSUP
     assert _decode(lib, pdt=3) == UNSUP
     assert _decode(lib, scale=0.0) == SHAPE
@@ -135,7 +135,7 @@ def test_merge_validation(lib):
 
 def test_binding_names_match_abi():
     for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache",
-              "mla_decode_sparse", "mla_sparse_split_count",
+              "mla_decode_sparse", "mla_sparse_split_count", "mla_decode_normal", "mla_normal_workspace_size",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
         assert callable(getattr(mk, n))
 
@@ -152,7 +152,7 @@ def test_append_validation(lib):
     assert _append(lib, dr=32) == UNSUP
     assert _append(lib, P=24) == UNSUP
     assert _append(lib, P=2048) == UNSUP
-    assert _append(lib, T=9) == UNSUP
+    assert _append(lib, T=1025) == UNSUP
     assert _append(lib, T=0) == SHAPE
     assert _append(lib, B=-1) == SHAPE
     assert _append(lib, nb=0) == SHAPE
@@ -177,7 +177,7 @@ def _sparse(lib, **kw):
 def test_sparse_validation(lib):
     assert _sparse(lib, r=256) == UNSUP
     assert _sparse(lib, dr=32) == UNSUP
-    assert _sparse(lib, T=9) == UNSUP
+    assert _sparse(lib, T=1025) == UNSUP
     assert _sparse(lib, H=129) == UNSUP
     assert _sparse(lib, P=24) == UNSUP
     assert _sparse(lib, odt=4) == UNSUP
@@ -202,3 +202,42 @@ def test_sparse_split_count(lib):
     assert lib.mla_sparse_split_count(0, 1, 128, 2048, 0, ctypes.byref(sc)) == OK and sc.value == 1
     assert lib.mla_sparse_split_count(64, 1, 128, 0, 0, ctypes.byref(sc)) == SHAPE
     assert lib.mla_sparse_split_count(64, 1, 128, 16, 0, None) == NULL
+
+
+def _normal(lib, **kw):
+    a = dict(qn=P16, qp=P16, wk=P16, wv=P16, kv=P16, nb=64, P=64, bt=P16, mb=64, sl=P16, B=2, T=1, H=128,
+             dn=128, dr=64, dv=128, r=512, maxL=4096, scale=0.07, chunk=1024, ws=P16, wsb=1 << 40, out=P16,
+             lse=None)
+    a.update(kw)
+    return lib.mla_decode_normal(a["qn"], a["qp"], a["wk"], a["wv"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"],
+                                 a["sl"], a["B"], a["T"], a["H"], a["dn"], a["dr"], a["dv"], a["r"], a["maxL"],
+                                 ctypes.c_float(a["scale"]), a["chunk"], a["ws"], ctypes.c_size_t(a["wsb"]),
+                                 a["out"], a["lse"], None)
+
+
+def test_normal_validation(lib):
+    assert _normal(lib, dn=64) == UNSUP
+    assert _normal(lib, r=256) == UNSUP
+    assert _normal(lib, T=1025) == UNSUP
+    assert _normal(lib, P=24) == UNSUP
+    assert _normal(lib, chunk=0) == SHAPE
+    assert _normal(lib, maxL=0) == SHAPE
+    assert _normal(lib, mb=63) == SHAPE
+    assert _normal(lib, scale=0.0) == SHAPE
+    assert _normal(lib, ws=None) == WS
+    assert _normal(lib, wsb=1000) == WS
+    assert _normal(lib, qn=P17) == ALIGN
+    assert _normal(lib, out=None) == NULL
+    assert _normal(lib, B=1 << 16, chunk=1 << 9) == UNSUP      # B * chunk > 2^24
+    assert _normal(lib, B=0, qn=None, out=None, ws=None) == OK
+
+
+def test_normal_workspace_size(lib):
+    nb = ctypes.c_size_t(0)
+    assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 4096, ctypes.byref(nb)) == OK
+    one = nb.value
+    # latent + rope + K + V, each rounded to 256 bytes; no carried state with one chunk
+    assert one == 4 * 4096 * (512 + 64 + 2 * 128 * 128) * 2
+    assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 1024, ctypes.byref(nb)) == OK
+    assert nb.value == one // 4 + 4 * 128 * 128 * 4 + 2 * (4 * 128 * 4)   # + output, max and sum state
+    assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 1024, None) == NULL
