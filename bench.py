@@ -150,6 +150,75 @@ def bench_sparse(name, K, W, R, dev):
     }
 
 
+def crossover(Ts, S_ctx, B, K, W, dev):
+    """Time the absorbed chain (absorb, latent attention with automatic splits,
+    merge, un-absorb) and the Normal path (gather, up-projection GEMMs, MHA
+    attention; one chunk) on the same seeded inputs for query blocks of T
+    tokens over S_ctx cached tokens (causal over the block).  Returns one
+    record per T and the model's MAC counts ("MLA in full detail", cost
+    analysis: Normal S*512*128*256 + 128*T*S*320, absorbed T*128*128*512*2 +
+    128*T*S*1088 multiply-adds per layer)."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    scale = mk.softmax_scale()
+    rows = []
+
+    def upload(case, dev):
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return dict(q_nope=bf16(case.q_nope), q_pe=bf16(case.q_pe), w_uk=bf16(case.w_uk), w_uv=bf16(case.w_uv),
+                    kv_cache=bf16(case.kv_cache), block_table=torch.from_numpy(case.block_table).to(dev),
+                    seqlens=torch.from_numpy(case.seqlens).to(dev))
+
+    for T in Ts:
+        wl = synth.Workload(f"xover_t{T}", B=B, T=T, H=128, L=S_ctx, page_size=64, seed=3000 + T)
+        case = synth.make_case(wl, poison=False)
+        d = upload(case, dev)
+        ws = torch.empty(max(mk.mla_normal_workspace_size(B, T, 128, S_ctx, S_ctx), 16), dtype=torch.uint8,
+                         device=dev)
+        n_out = torch.empty((B, T, 128, 128), dtype=torch.float32, device=dev)
+        n_lse = torch.empty((B, T, 128), dtype=torch.float32, device=dev)
+        buf = mk.DecodeBuffers(B, T, 128, S_ctx, 64, 0, dev, part_dtype=torch.bfloat16)
+
+        def absorbed():
+            return mk.absorbed_decode(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"],
+                                      d["block_table"], d["seqlens"], S_ctx, num_splits=0, buffers=buf)
+
+        def normal():
+            return mk.mla_decode_normal(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"],
+                                        d["block_table"], d["seqlens"], S_ctx, scale, chunk=S_ctx, workspace=ws,
+                                        out=n_out, lse=n_lse)
+
+        res = {}
+        for name, fn in (("absorbed", absorbed), ("normal", normal)):
+            for _ in range(W):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(K):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / K
+        a_out, _ = absorbed()
+        n_o, _ = normal()
+        torch.cuda.synchronize()
+        diff = float((a_out - n_o).abs().max())
+        ref = float(n_o.abs().max())
+        macs_normal = S_ctx * 512 * 128 * 256 + 128 * T * S_ctx * 320
+        macs_absorbed = T * 128 * 128 * 512 * 2 + 128 * T * S_ctx * 1088
+        rows.append({"T": T, "S": S_ctx, "B": B, "H": 128, "absorbed_ms": res["absorbed"],
+                     "normal_ms": res["normal"], "normal_over_absorbed": res["normal"] / res["absorbed"],
+                     "model_macs_normal_per_seq": macs_normal, "model_macs_absorbed_per_seq": macs_absorbed,
+                     "max_abs_diff": diff, "max_abs_out": ref})
+        del d, ws, n_out, n_lse, buf
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(case, pairs_n, threads, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys)."""
@@ -196,6 +265,12 @@ def main():
                     help="skip the sparse (top-k) decode measurement reported under detail")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="instead of the benchmark line: time the absorbed and the Normal path over query-block "
+                         "lengths T (one JSON line per T)")
+    ap.add_argument("--crossover-T", default="1,8,32,64,96,128,160,192,256,384,512")
+    ap.add_argument("--crossover-S", type=int, default=4096)
+    ap.add_argument("--crossover-B", type=int, default=4)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -211,6 +286,12 @@ def main():
 
     mk.load_library()
     dev = "cuda:0"
+    if args.crossover:
+        Ts = [int(x) for x in args.crossover_T.split(",")]
+        for row in crossover(Ts, args.crossover_S, args.crossover_B, max(3, min(args.steps, 20)),
+                             max(1, min(args.warmup, 3)), dev):
+            print(json.dumps(row), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     case = synth.make_case(wl, poison=False)
     B, T, H = case.B, case.T, case.H

@@ -119,6 +119,11 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
  *               chunks may be empty); chunk s writes its partial state to row
  *               split_indptr[b] + s of part_out / part_lse.
  *               0: automatic split counts (see mla_decode_workspace_size).
+ *               When out_latent is given and B*ceil(T*H/128) work units already
+ *               reach the CU count, the automatic rule gives every sequence
+ *               one chunk and the call runs unsplit: out_latent and lse are
+ *               written directly, the partial buffers and split_indptr are not
+ *               touched.
  *   workspace   device scratch of the size reported by mla_decode_workspace_size
  *               (the automatic mode's work list); may be NULL when that size is 0.
  *               Contents on entry are ignored.

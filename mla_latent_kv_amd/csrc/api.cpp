@@ -213,6 +213,14 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = (hipStream_t)stream;
 
+  if (num_splits == 0 && out_latent) {
+    // automatic mode with the merged result wanted: when one work unit per
+    // sequence already fills every CU, the rule gives each sequence a single
+    // chunk, so run unsplit (no partials, no merge)
+    int cus = 0;
+    if ((st = device_cus(&cus))) return st;
+    if ((long long)B * n_rg >= cus) num_splits = 1;
+  }
   if (num_splits == 1) {
     if ((st = check_ptr16(out_latent))) return st;
     p.out = out_latent;

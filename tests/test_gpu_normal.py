@@ -93,3 +93,27 @@ def test_normal_equals_absorbed_full_workload(mk):
     assert_close(to_f64(n_out)[b, :, h], ref[b, :, h], "normal out vs oracle")
     assert_close(to_f64(n_out), to_f64(a_out), "normal vs absorbed out")
     assert_close(to_f64(n_lse), to_f64(a_lse), "normal vs absorbed lse")
+
+
+def test_absorbed_automatic_runs_unsplit_when_units_fill_the_chip(mk):
+    """num_splits = 0 with 4 x 64 query tokens x 128 heads: 256 work units
+    already reach the CU count, so the call runs unsplit (partials untouched)
+    and still matches the oracle."""
+    import torch
+    log("[absorbed] automatic mode at B*ceil(T*H/128) >= CUs")
+    case = synth.make_case(synth.scaled(W["v3_b64_l4096"], B=4, T=64, L=300, seed=2405))
+    d = upload(case)
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, 0, "cuda:0")
+    buf.split_indptr.fill_(-7)
+    q_lat = mk.mla_absorb_q(d["q_nope"], d["w_uk"])
+    lat, lse = mk.mla_decode_latent(q_lat, d["q_pe"], d["kv_cache"], d["block_table"], d["seqlens"],
+                                    case.max_seqlen, SCALE, num_splits=0, out_dtype=torch.float32, buffers=buf)
+    out = mk.mla_unabsorb_out(lat, d["w_uv"])
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if case.B * case.T * case.H // 128 >= cus:
+        assert (buf.split_indptr.cpu().numpy() == -7).all()
+    pairs, ref, ref_lse = _ref(case, n_pairs=24)
+    b, h = pairs[:, 0], pairs[:, 1]
+    assert_close(to_f64(out)[b, :, h], ref[b, :, h], "absorbed auto-unsplit out")
+    assert_close(to_f64(lse)[b, :, h], ref_lse[b, :, h], "absorbed auto-unsplit lse")
