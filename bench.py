@@ -235,6 +235,20 @@ def cpu_baseline(case, pairs_n, threads, seed=123):
     keys_sample = float(np.sum(case.seqlens[pairs[:, 0]]))
     keys_all = float(np.sum(case.seqlens)) * H
     t_full = dt * keys_all / keys_sample
+    # the fp64 absorbed mirror (absorb, latent attention, un-absorb) on the whole batch
+    t0 = time.perf_counter()
+    ql = oracle.absorb(case.q_nope, case.w_uk)
+    lat, _ = oracle.latent_attention(case, ql, nthreads=threads)
+    oracle.unabsorb(lat, case.w_uv)
+    t_mirror = time.perf_counter() - t0
+    cpu = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": case.B * case.T / t_full,
         "unit": "tokens/s",
@@ -242,15 +256,18 @@ def cpu_baseline(case, pairs_n, threads, seed=123):
         "kind": "oracle",
         "sample": f"fp64 Normal-path oracle on {len(pairs)} of {B * H} (sequence, head) pairs "
                   f"({int(keys_sample)} keys, {dt:.1f} s on {threads} threads), scaled linearly "
-                  f"to all {B * H} pairs",
+                  f"to all {B * H} pairs; {cpu}, {os.cpu_count()} logical CPUs visible",
+        "absorbed_mirror_value": case.B * case.T / t_mirror,
+        "absorbed_mirror_sample": f"fp64 absorbed mirror (absorb, latent attention, un-absorb) on the whole "
+                                  f"batch: {t_mirror:.1f} s on {threads} threads",
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--splits", type=int, default=4,
                     help="split-KV chunks per sequence (0 = automatic)")
@@ -355,6 +372,14 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     dec_ms_avg = float(np.mean(dec_ms))
 
+    # the same with one cache replica (no rotation: the 256 MB last-level cache
+    # may serve part of a step's reads from the previous step) -- context only
+    warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        step(0, warm[i])
+    torch.cuda.synchronize()
+    warm_ms = float(np.median([a.elapsed_time(b) for a, b in warm]))
+
     # whole chain: one captured HIP graph per cache replica (the four launches of
     # a step as graph nodes), replayed back to back
     ms_per_step = eager_ms_per_step
@@ -446,6 +471,11 @@ def main():
         "detail": {
             "kernel": "decode_kernel (latent attention, split-KV partials)",
             "decode_us": dec_ms_avg * 1e3,
+            "decode_us_median": float(np.median(dec_ms)) * 1e3,
+            "decode_us_p10": float(np.percentile(dec_ms, 10)) * 1e3,
+            "decode_us_p90": float(np.percentile(dec_ms, 90)) * 1e3,
+            "decode_us_warm_median": warm_ms * 1e3,
+            "context_rows_per_s": float(np.sum(case.seqlens)) / (dec_ms_avg * 1e-3),
             "decode_us_min": float(np.min(dec_ms)) * 1e3,
             "decode_alg_bytes": dec_bytes,
             "decode_alg_flops": dec_flops,
