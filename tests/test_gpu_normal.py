@@ -1,9 +1,9 @@
 """GPU parity of the Normal path (mla_decode_normal: per-head up-projected K/V,
 chunked over the cache) against the oracle's fp64 Normal path, for one chunk
 and for several (the carried max/sum/output state), ragged lengths, causal
-multi-token rows up to T = 64 and 16 to 128 heads; plus the absorbed chain at
-T = 64 (the same function in the other association order) against the same
-oracle."""
+multi-token rows up to T = 130 (two query tiles per head) and 2 to 128 heads;
+plus the absorbed chain at T = 64 and 130 (the same function in the other
+association order) against the same oracle."""
 import numpy as np
 import pytest
 
@@ -31,6 +31,8 @@ CASES = {
     "mtp_t4_h32": synth.scaled(W["v3_mtp_b32_t4_h32"], B=3, lengths=(100, 4, 77), seed=2403),
     "t64_h16_p16": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, T=64, H=16, page_size=16, lengths=(64, 300),
                                 seed=2404),
+    # 130 query tokens: two 128-row query tiles per head, the second with 2 rows
+    "t130_h2": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, T=130, H=2, lengths=(130, 333), seed=2406),
 }
 
 
@@ -58,11 +60,12 @@ def test_normal_parity(mk, name, chunk):
     assert np.isfinite(got).all()
 
 
-def test_absorbed_chain_t64(mk):
-    """The absorbed path at T = 64 (a prefill-sized block of query tokens)."""
+@pytest.mark.parametrize("name", ["t64_h16_p16", "t130_h2"])
+def test_absorbed_chain_large_t(mk, name):
+    """The absorbed path at prefill-sized blocks of query tokens."""
     import torch
-    log("[absorbed] t64_h16_p16 splits 1 and 3")
-    case = synth.make_case(CASES["t64_h16_p16"])
+    log(f"[absorbed] {name} splits 1 and 3")
+    case = synth.make_case(CASES[name])
     d = upload(case)
     pairs, ref, ref_lse = _ref(case)
     b, h = pairs[:, 0], pairs[:, 1]
@@ -71,8 +74,8 @@ def test_absorbed_chain_t64(mk):
                                       d["block_table"], d["seqlens"], case.max_seqlen, num_splits=splits,
                                       latent_dtype=torch.float32)
         torch.cuda.synchronize()
-        assert_close(to_f64(out)[b, :, h], ref[b, :, h], f"absorbed t64 S={splits} out")
-        assert_close(to_f64(lse)[b, :, h], ref_lse[b, :, h], f"absorbed t64 S={splits} lse")
+        assert_close(to_f64(out)[b, :, h], ref[b, :, h], f"absorbed {name} S={splits} out")
+        assert_close(to_f64(lse)[b, :, h], ref_lse[b, :, h], f"absorbed {name} S={splits} lse")
 
 
 def test_normal_equals_absorbed_full_workload(mk):
