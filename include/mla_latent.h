@@ -22,7 +22,9 @@
  *
  * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
  * written at their paged positions before the decode that reads them); for
- * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent.
+ * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent;
+ * for comparison, mla_decode_normal (the same function in the Normal,
+ * per-head up-projected association order).
  *
  * "M5.8" is the page "M5.8 - Multi-Head Latent Attention: Latent KV State,
  * Weight Absorption, and FlashMLA"; "mlxcel" is its "MLA absorbed decode" page.
@@ -30,12 +32,15 @@
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers to caller-owned, row-major, contiguous
  *    memory.  bf16 tensors are passed as uint16_t storage of bfloat16 values.
- *    Every pointer must be 16-byte aligned.
+ *    Tensor pointers must be 16-byte aligned; int32 index arrays and fp32 lse
+ *    arrays 4-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *    validate host-side scalars and pointers, enqueue their kernels on `stream`
  *    and return; they never synchronise, never allocate device memory and keep
- *    no state between calls.  Calls on different streams that share no output
- *    buffer may run concurrently.
+ *    no state between calls -- except mla_validate_inputs (synchronous, for
+ *    debugging) and mla_decode_normal (rocBLAS keeps a handle per device).
+ *    Calls on different streams that share no output or workspace buffer may
+ *    run concurrently.
  *  - The return value is MLA_OK or a negative mla_status.  On a negative return
  *    nothing has been enqueued, except MLA_ERR_LAUNCH, which reports a failed
  *    kernel launch (hipGetLastError) after validation passed.
