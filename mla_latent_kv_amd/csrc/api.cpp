@@ -64,10 +64,11 @@ size_t plan_bytes(long long max_items) { return 256 + (size_t)max_items * 16; }
 std::mutex g_blas_mu;
 rocblas_handle g_blas[64] = {};
 
+// (the caller holds g_blas_mu: a handle's stream is set per call, so host
+// threads that share the device's handle take turns enqueueing)
 int blas_handle(rocblas_handle* h) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MLA_ERR_LAUNCH;
-  std::lock_guard<std::mutex> lock(g_blas_mu);
   if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) return MLA_ERR_LAUNCH;
   *h = g_blas[dev];
   return MLA_OK;
@@ -417,6 +418,7 @@ int mla_decode_normal(const uint16_t* q_nope, const uint16_t* q_pe, const uint16
   const NormalLayout wl = normal_layout(B, T, H, chunk, n_chunks > 1);
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
+  std::lock_guard<std::mutex> lock(g_blas_mu);
   rocblas_handle bh = nullptr;
   if ((st = blas_handle(&bh))) return st;
   if (rocblas_set_stream(bh, s) != rocblas_status_success) return MLA_ERR_LAUNCH;
