@@ -55,6 +55,14 @@ def small_cases():
                                        seed=2111),
         # the largest multi-token decode the boundary takes (T = 8), 8 x 16 = 128 rows
         "t8_h16": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, T=8, H=16, lengths=(8, 300), seed=2112),
+        # the largest page size the boundary takes (one partial second page)
+        "page1024_h8": synth.scaled(W["v3_b64_l4096"], B=2, H=8, page_size=1024, lengths=(1500, 1024),
+                                    seed=2113),
+        # many tiny sequences (1..40 tokens): more work units than CUs, most of them one step
+        "b300_tiny_h4": synth.scaled(W["v3_b64_l4096"], B=300, H=4,
+                                     lengths=tuple(1 + (7 * i) % 40 for i in range(300)), seed=2114),
+        # the largest query block the boundary takes: T = 1024 rows of one head, 8 row groups
+        "t1024_h1": synth.scaled(W["v3_mtp_b32_t4_h32"], B=1, T=1024, H=1, lengths=(1100,), seed=2115),
     }
 
 
@@ -135,7 +143,7 @@ def test_end_to_end_vs_normal_path(mk, name):
 @pytest.mark.parametrize("part", ["f32", "bf16"])
 @pytest.mark.parametrize("S", [2, 3, 7])
 @pytest.mark.parametrize("name", ["v3_ragged_b5", "mtp_t4_h32", "page16_h64", "mtp_p16_tail", "history_matrix",
-                                  "t8_h16"])
+                                  "t8_h16", "page1024_h8", "b300_tiny_h4"])
 def test_split_partials_and_merge(mk, name, S, part):
     import torch
     log(f"[split] {name} S={S} partials={part}")
