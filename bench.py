@@ -423,6 +423,23 @@ def main():
     app_ms = app_ev[0].elapsed_time(app_ev[1]) / K
     app_bytes = 2 * B * T * (512 + 64) * 2 + 4 * B * 2   # rows read + written, seqlens, table entries
 
+    # context line: the chip's practical streaming rate on a plain 1 GiB
+    # device-to-device copy (read + written bytes over its duration)
+    src_c = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst_c = torch.empty_like(src_c)
+    src_c.fill_(1)
+    for _ in range(2):
+        dst_c.copy_(src_c)
+    ce = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ce[0].record(stream)
+    for _ in range(5):
+        dst_c.copy_(src_c)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = 2 * (1 << 30) * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del src_c, dst_c
+    torch.cuda.empty_cache()
+
     if args.copy_calibration:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
         # factor that turns those counters into bytes for the decode kernel
@@ -477,6 +494,7 @@ def main():
             "decode_us_warm_median": warm_ms * 1e3,
             "context_rows_per_s": float(np.sum(case.seqlens)) / (dec_ms_avg * 1e-3),
             "decode_us_min": float(np.min(dec_ms)) * 1e3,
+            "hbm_copy_GBps": copy_GBps,
             "decode_alg_bytes": dec_bytes,
             "decode_alg_flops": dec_flops,
             "decode_tflops": dec_flops / (dec_ms_avg * 1e-3) / 1e12,
