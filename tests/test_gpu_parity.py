@@ -126,14 +126,17 @@ def test_unabsorb(mk, name, latent_f32):
     assert_close(to_f64(out), ref, "out")
 
 
+@pytest.mark.parametrize("S", [1, 4])
 @pytest.mark.parametrize("name", sorted(CASES))
-def test_end_to_end_vs_normal_path(mk, name):
+def test_end_to_end_vs_normal_path(mk, name, S):
+    """S = 1: absorb, decode, un-absorb; S = 4: absorb, split decode, merge,
+    un-absorb."""
     import torch
-    log(f"[end-to-end] {name}")
+    log(f"[end-to-end] {name} S={S}")
     case = _case(name)
     d = upload(case)
     out, lse = mk.absorbed_decode(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["kv_cache"],
-                                  d["block_table"], d["seqlens"], case.max_seqlen)
+                                  d["block_table"], d["seqlens"], case.max_seqlen, num_splits=S)
     torch.cuda.synchronize()
     ref, ref_lse = oracle.normal_decode(case)
     assert_close(to_f64(out), ref, "out")
