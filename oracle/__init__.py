@@ -13,6 +13,10 @@ Two independent CPU implementations live here:
   split partials, merge, un-absorb).  Its header cites the passages followed.
 * ``expanded_attention_f64`` / ``absorbed_attention_f64`` below: small numpy
   float64 versions for tiny inputs, used to pin the C code.
+* ``e4m3fn_decode`` / ``bf16_round`` / ``fp8_rows_to_bf16``: the FP8 cache
+  row (M5.8 0x0B) dequantized to the bf16 rows the stages above read; pinned
+  to PyTorch's float8_e4m3fn conversion, the encoding's closed forms, a
+  hand-built row and single rounding at constructed ties.
 
 Pages ("MLA in full detail", mlinterviewnotes; "M5.8 - Multi-Head Latent
 Attention", transformer-system) define the computation; every stage function
@@ -316,3 +320,66 @@ def expanded_attention_f64(case, scale=None):
         out[b] = np.einsum("thj,jhv->thv", p, V)
         lse[b] = (m + np.log(l))[..., 0]
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache rows (M5.8 0x0B, "Exact 656-byte FP8 row"): 512 E4M3 latent
+# values, four fp32 scales, 64 bf16 rope values; the decode dequantizes the
+# latent to bf16 and attends in bf16.  Row bytes: [0, 512) the code of latent
+# column c at byte c, [512, 528) scale g (little-endian fp32) of columns
+# [128 g, 128 g + 128) -- one scale per 128 latent values --, [528, 656) rope.
+
+def e4m3fn_decode(codes):
+    """Values (float64) of E4M3 codes in the OCP FP8 encoding (the one called
+    E4M3FN): sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+    field 0 holds the subnormals (m / 8) * 2^-6; no infinities; exponent and
+    mantissa all ones is NaN (largest finite magnitude 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = c >> 7
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def bf16_round(x):
+    """float64 -> bf16 bits, round to nearest even in one step (no detour
+    through float32, whose own rounding could land on a bf16 tie).  Finite
+    nonzero magnitudes must lie in bf16's normal range; NaN stays NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any((a != 0) & np.isfinite(a) & ((a < 2.0 ** -126) | (a >= 2.0 ** 128))):
+        raise ValueError("bf16_round: value outside bf16's normal range")
+    u = x.view(np.uint64)
+    # keep 7 of the 52 fraction bits: add half an ulp minus one, plus the kept lsb
+    drop = np.uint64(45)
+    lsb = (u >> drop) & np.uint64(1)
+    r = (u + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + lsb) >> drop << drop
+    y = r.view(np.float64).astype(np.float32)      # exact: 8 significant bits
+    bits = (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits)
+
+
+def fp8_rows_to_bf16(kv_fp8):
+    """Dequantize FP8 rows [..., 656] to bf16 rows [..., 576] (bits): latent
+    column c becomes bf16(e4m3(code_c) * scale[c // 128]) -- the exact
+    product, rounded once --, and the rope values are copied."""
+    rows = np.asarray(kv_fp8, dtype=np.uint8)
+    if rows.shape[-1] != 656:
+        raise ValueError("an FP8 row is 656 bytes")
+    lead = rows.shape[:-1]
+    codes = rows[..., :512]
+    scales = np.ascontiguousarray(rows[..., 512:528]).view("<f4").astype(np.float64)   # [..., 4]
+    vals = e4m3fn_decode(codes).reshape(lead + (4, 128)) * scales[..., :, None]
+    out = np.empty(lead + (576,), dtype=np.uint16)
+    out[..., :512] = bf16_round(vals.reshape(lead + (512,)))
+    out[..., 512:] = np.ascontiguousarray(rows[..., 528:]).view("<u2")
+    return out
+
+
+def fp8_case_as_bf16(fcase):
+    """The decode case whose bf16 cache holds the dequantized FP8 rows: every
+    oracle stage above then applies unchanged."""
+    import dataclasses
+    return dataclasses.replace(fcase.case, kv_cache=fp8_rows_to_bf16(fcase.kv_fp8))

@@ -403,3 +403,58 @@ def make_sparse(wl: Workload, topk: int, valid: Optional[tuple] = None, poison: 
     flat[sel] = _normal_bf16(rng, (sel.shape[0], r + dr))
     return SparseCase(wl, q_lat, q_pe, kv_cache, indices, nv.astype(np.int32) if use_length else None,
                       seqlens, block_table)
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache rows (M5.8 0x0B, "Exact 656-byte FP8 row": 512 one-byte E4M3
+# latent values, four fp32 scales, 64 bf16 rope values per row).  The pages
+# give the three segments and their sizes but not their order inside the row;
+# they are stored in the order listed:
+#     bytes [0, 512)    E4M3 code of latent column c at byte c
+#     bytes [512, 528)  scale g (little-endian fp32) of columns [128 g, 128 g + 128)
+#     bytes [528, 656)  the 64 rope values (bf16)
+FP8_ROW_BYTES = 656
+FP8_NAN_CODE = np.uint8(0x7F)   # E4M3FN: exponent and mantissa all ones
+F32_NAN_BITS = np.uint32(0x7FC00000)
+
+
+@dataclasses.dataclass
+class Fp8Case:
+    """A decode workload over an FP8 cache: ``case`` supplies queries,
+    weights, block table and lengths (its bf16 ``kv_cache`` is not read by
+    the FP8 path); ``kv_fp8`` holds the rows."""
+    case: Case
+    kv_fp8: np.ndarray   # [num_blocks, P, 656] uint8
+
+
+def make_fp8_case(wl: Workload, poison: bool = True) -> Fp8Case:
+    """``make_case(wl)`` for everything but the latent part of the rows, then,
+    from a second generator seeded ``wl.seed + 0xF8``:
+
+    1. latent codes [num_blocks, P, 512]: magnitude code
+       clip(round(N(108, 10^2)), 0, 126) (the 127 finite E4M3 magnitudes in
+       increasing order; 108 encodes 96), sign bit uniform;
+    2. scales [num_blocks, P, 4] = 2^U(-10, -6) rounded to float32;
+    3. rope values: columns 512..575 of ``make_case``'s bf16 rows.
+
+    With ``poison``, every row no sequence may read holds NaN codes, NaN
+    scales and the bf16 NaN rope values of ``make_case``."""
+    case = make_case(wl, poison=poison)
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 0xF8))
+    nb, P = case.kv_cache.shape[0], wl.page_size
+    r = wl.r
+    if r != 512 or wl.d_rope != 64:
+        raise ValueError("the FP8 row holds 512 latent and 64 rope values")
+    mag = np.clip(np.rint(rng.normal(108.0, 10.0, size=(nb, P, r))), 0, 126).astype(np.uint8)
+    sign = rng.integers(0, 2, size=(nb, P, r), dtype=np.uint8) << np.uint8(7)
+    codes = mag | sign
+    scales = np.exp2(rng.uniform(-10.0, -6.0, size=(nb, P, 4))).astype(np.float32)
+    rows = np.empty((nb, P, FP8_ROW_BYTES), dtype=np.uint8)
+    rows[:, :, :512] = codes
+    rows[:, :, 512:528] = scales.astype("<f4").view(np.uint8).reshape(nb, P, 16)
+    rows[:, :, 528:] = np.ascontiguousarray(case.kv_cache[:, :, r:]).astype("<u2").view(np.uint8).reshape(nb, P, 128)
+    if poison:
+        dead = np.isnan(bf16_bits_to_f32(case.kv_cache[:, :, r]))   # rows make_case poisoned
+        rows[dead, :512] = FP8_NAN_CODE
+        rows[dead, 512:528] = np.full(4, F32_NAN_BITS, dtype="<u4").view(np.uint8)
+    return Fp8Case(case, rows)

@@ -618,3 +618,120 @@ def test_sparse_logical_ids_negative_control():
                     wrong[b, t, k] = sc.block_table[b, j // P] * P + j % P
     bad, _ = _sparse(sc, indices=wrong)
     assert _fails(bad, lat)
+
+
+# --------------------------------------------------------------------------
+# 9. FP8 cache rows (M5.8 0x0B, "Exact 656-byte FP8 row")
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    """Every one of the 256 codes against PyTorch's float8_e4m3fn conversion
+    (an independent implementation of the OCP E4M3 encoding)."""
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3fn_decode(codes)
+    assert np.array_equal(got, want, equal_nan=True)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_e4m3_closed_forms():
+    """Values fixed by the encoding: bias 7, subnormal step 2^-9, largest
+    finite 448, NaN at exponent and mantissa all ones, sign in bit 7."""
+    d = oracle.e4m3fn_decode
+    assert d(0x38) == 1.0 and d(0x40) == 2.0 and d(0x30) == 0.5
+    assert d(0x39) == 1.125 and d(0x3F) == 1.875
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x08) == 2.0 ** -6
+    assert d(0x00) == 0.0 and d(0x80) == 0.0 and np.signbit(d(0x80))
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x77) == 240.0 and not np.isnan(d(0x78))      # exponent 15 is finite but for m = 7
+
+
+def test_bf16_round_nearest_even_and_single_rounding():
+    """Ties go to the even neighbour; a value just above a tie goes up even
+    when the excess is below float32's precision (a detour through float32
+    would land on the tie and go down)."""
+    got = oracle.bf16_round(np.array([1 + 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -40, 1 + 3 * 2.0 ** -8,
+                                      -(1 + 3 * 2.0 ** -8), 1 + 2.0 ** -9, -2.5, 0.0, np.nan]))
+    assert list(got[:7]) == [0x3F80, 0x3F81, 0x3F82, 0xBF82, 0x3F80, 0xC020, 0x0000]
+    assert np.isnan(synth.bf16_bits_to_f32(got[7:]))
+    # on float32 inputs it agrees with the float32 -> bf16 encoder of the input recipe
+    x = np.random.default_rng(5).standard_normal(20000).astype(np.float32) * np.float32(37.0)
+    assert np.array_equal(oracle.bf16_round(x.astype(np.float64)), synth.f32_to_bf16_bits(x))
+
+
+def test_fp8_product_rounded_once():
+    """e4m3(code) * scale is rounded to bf16 from its exact value: for codes
+    and fp32 scales whose exact product lies within float32's half ulp above
+    a bf16 tie, the result is the upper neighbour (a detour through float32
+    would land on the tie and round to even)."""
+    hits = []
+    for code in range(0x39, 0x40):                     # 1.125 .. 1.875
+        v = float(oracle.e4m3fn_decode(code))
+        for i in range(128):
+            mid = 1.0 + (2 * i + 1) * 2.0 ** -8         # tie between two bf16 values in [1, 2)
+            s0 = np.float32(mid / v)
+            for s in (np.nextafter(s0, np.float32(0)), s0, np.nextafter(s0, np.float32(2))):
+                p = v * float(s)                         # exact (4 x 24 significant bits)
+                if p > mid and float(np.float32(p)) == mid:
+                    hits.append((code, s, mid + 2.0 ** -8))
+    assert len(hits) >= 4
+    for code, s, upper in hits:
+        row = np.zeros((1, 656), dtype=np.uint8)
+        row[0, :512] = code
+        row[0, 512:528] = np.full(4, s, dtype="<f4").view(np.uint8)
+        out = oracle.fp8_rows_to_bf16(row)
+        assert (synth.bf16_bits_to_f32(out[0, :512]) == upper).all()
+
+
+def test_fp8_row_layout_hand_built():
+    """Codes at bytes [0, 512), four little-endian fp32 scales at [512, 528)
+    each covering 128 consecutive latent columns, 64 bf16 rope values at
+    [528, 656)."""
+    row = np.zeros((2, 656), dtype=np.uint8)
+    row[:, :512] = 0x38                                # 1.0
+    row[1, 5] = 0xB0                                   # -0.5
+    row[:, 512:528] = np.array([1.0, 2.0, 4.0, 8.0], dtype="<f4").view(np.uint8)
+    row[:, 528:] = np.full(64, 0x3F00, dtype="<u2").view(np.uint8)       # 0.5
+    vals = synth.bf16_bits_to_f32(oracle.fp8_rows_to_bf16(row)).astype(np.float64)
+    want = np.concatenate([np.repeat([1.0, 2.0, 4.0, 8.0], 128), np.full(64, 0.5)])
+    assert np.array_equal(vals[0], want)
+    want[5] = -0.5
+    assert np.array_equal(vals[1], want)
+
+
+def test_fp8_dequant_matches_torch_when_float32_is_exact():
+    """With scales of at most 12 significant bits the product is exact in
+    float32, so PyTorch's float8 -> float32 -> bf16 route is a second
+    implementation of the same rounding."""
+    rng = np.random.default_rng(11)
+    n = 300
+    codes = rng.integers(0, 256, size=(n, 512), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                      # no NaN codes
+    sc = np.round(rng.uniform(2048, 4095, size=(n, 4))) * np.exp2(rng.integers(-20, -8, size=(n, 4)))
+    sc = sc.astype(np.float32)
+    rows = np.zeros((n, 656), dtype=np.uint8)
+    rows[:, :512] = codes
+    rows[:, 512:528] = sc.astype("<f4").view(np.uint8)
+    rows[:, 528:] = rng.integers(0, 256, size=(n, 128), dtype=np.uint8)
+    got = oracle.fp8_rows_to_bf16(rows)
+    lat = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+    prod = lat.view(n, 4, 128) * torch.from_numpy(sc)[:, :, None]
+    want = prod.reshape(n, 512).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[:, :512], want)
+    assert np.array_equal(got[:, 512:], rows[:, 528:].copy().view("<u2"))
+
+
+def test_fp8_case_reads_like_its_dequantized_bf16_case():
+    """The FP8 decode is the bf16 decode of the dequantized rows; the rows no
+    sequence reads stay NaN after dequantization, the live rows finite."""
+    wl = synth.Workload("f8", B=2, T=1, H=2, L=0, page_size=16, seed=77, lengths=(40, 17))
+    f = synth.make_fp8_case(wl)
+    bc = oracle.fp8_case_as_bf16(f)
+    live = np.zeros(bc.kv_cache.shape[:2], dtype=bool)
+    for b in range(bc.B):
+        for j in range(int(bc.seqlens[b])):
+            live[bc.block_table[b, j // 16], j % 16] = True
+    vals = synth.bf16_bits_to_f32(bc.kv_cache)
+    assert np.isfinite(vals[live]).all() and np.isnan(vals[~live]).all()
+    out, lse = oracle.normal_decode(bc)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
