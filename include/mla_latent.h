@@ -157,6 +157,27 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
                       void* out_latent, mla_dtype out_dtype, float* lse, void* stream);
 
+/* mla_decode_latent over a cache of FP8 rows (M5.8 0x0B, "Exact 656-byte FP8
+ * row"): every argument and result as there, except
+ *   kv_cache    [num_blocks,page_size,656] bytes, 16-byte aligned; row =
+ *               bytes [0,512) the E4M3 codes (OCP encoding, the one called
+ *               E4M3FN) of latent columns 0..511, bytes [512,528) four
+ *               little-endian fp32 scales, scale g covering columns
+ *               [128g, 128g+128), bytes [528,656) the 64 bf16 rope values.
+ * The latent is dequantized to bf16 in the kernel, c = bf16(code * scale)
+ * (the product formed in fp32, then rounded to nearest even), and the
+ * attention runs in bf16 as for bf16 rows.  The pages give the three
+ * segments and their sizes, not their order; the order above is the one
+ * they are listed in.  Codes of rows no query may see are never converted
+ * into a result (NaN codes or scales there are harmless). */
+int mla_decode_latent_fp8(const uint16_t* q_lat, const uint16_t* q_pe, const uint8_t* kv_cache,
+                          int num_blocks, int page_size, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
+                          int d_R, int max_seqlen, float softmax_scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* part_out,
+                          mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                          void* out_latent, mla_dtype out_dtype, float* lse, void* stream);
+
 /* Split count of mla_decode_sparse: num_splits > 0 is returned as is; 0 picks
  * S = clamp(floor(CUs / (B*T*ceil(H/128))), 1, ceil(topk/256)) (and at most
  * 128), enough work units for every CU with chunks of at least 256 entries.

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
 
 * ``mla_absorb_q``      q~ = W_UK^T q_nope                   ("MLA in full detail", Step 2)
 * ``mla_decode_latent`` latent attention over the paged cache ("MLA in full detail", Step 3)
+* ``mla_decode_latent_fp8``  the same over 656-byte FP8 rows    (M5.8 0x0B)
 * ``mla_merge_splits``  log-sum-exp merge of split partials   (M5.8 0x0C)
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
 * ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
@@ -58,6 +59,7 @@ def load_library():
     L.mla_decode_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ), ctypes.POINTER(I)]
     L.mla_decode_latent.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I,
                                     P, SZ, P, I, P, P, P, I, P, P]
+    L.mla_decode_latent_fp8.argtypes = L.mla_decode_latent.argtypes
     L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
@@ -70,7 +72,7 @@ def load_library():
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
                  "mla_decode_sparse", "mla_normal_workspace_size", "mla_decode_normal",
-                 "mla_validate_inputs"):
+                 "mla_validate_inputs", "mla_decode_latent_fp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -156,6 +158,23 @@ def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, s
 
     Returns (out_latent, lse).  With num_splits != 1 and merge=False the merge
     is skipped, out_latent is None and the partials stay in ``buffers``."""
+    return _decode(False, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                   num_splits, out_dtype, buffers, out_latent, lse, merge, stream)
+
+
+def mla_decode_latent_fp8(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                          num_splits=1, out_dtype=None, buffers: Optional[DecodeBuffers] = None,
+                          out_latent=None, lse=None, merge=True, stream=None):
+    """mla_decode_latent over FP8 rows: ``kv_cache`` is uint8 [num_blocks, P, 656]."""
+    torch = _torch()
+    if kv_cache.dtype != torch.uint8 or kv_cache.shape[-1] != 656:
+        raise ValueError("mla_decode_latent_fp8: kv_cache must be uint8 [num_blocks, page_size, 656]")
+    return _decode(True, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                   num_splits, out_dtype, buffers, out_latent, lse, merge, stream)
+
+
+def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+            num_splits, out_dtype, buffers, out_latent, lse, merge, stream):
     torch = _torch()
     B, T, H, r = q_lat.shape
     dr = q_pe.shape[3]
@@ -170,7 +189,8 @@ def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, s
     if num_splits != 1 and buffers is None:
         buffers = DecodeBuffers(B, T, H, max_seqlen, page_size, num_splits, q_lat.device)
     ws = buffers.workspace if num_splits != 1 else None
-    st = load_library().mla_decode_latent(
+    lib = load_library()
+    st = (lib.mla_decode_latent_fp8 if fp8 else lib.mla_decode_latent)(
         _ptr(q_lat), _ptr(q_pe), _ptr(kv_cache), num_blocks, page_size, _ptr(block_table),
         max_blocks, _ptr(seqlens), B, T, H, r, dr, int(max_seqlen), float(softmax_scale),
         int(num_splits), _ptr(ws), buffers.workspace_bytes if num_splits != 1 else 0,
@@ -180,7 +200,7 @@ def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, s
         _ptr(buffers.split_indptr if num_splits != 1 else None),
         _ptr(out_latent if want_out else None), _dtype_code(out_dtype),
         _ptr(lse if want_out else None), _stream(stream))
-    _check(st, "mla_decode_latent")
+    _check(st, "mla_decode_latent_fp8" if fp8 else "mla_decode_latent")
     return (out_latent, lse) if want_out else (None, None)
 
 
@@ -350,7 +370,7 @@ def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, ma
 
 __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
-    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_merge_splits",
+    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
     "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
     "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",

@@ -174,13 +174,14 @@ int mla_decode_workspace_size(int B, int T, int H, int r, int max_seqlen, int pa
   return MLA_OK;
 }
 
-int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
-                      int num_blocks, int page_size, const int32_t* block_table,
-                      int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
-                      int d_R, int max_seqlen, float softmax_scale, int num_splits,
-                      void* workspace, size_t workspace_bytes, void* part_out,
-                      mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
-                      void* out_latent, mla_dtype out_dtype, float* lse, void* stream) {
+// dense decode over bf16 rows (fp8 false) or FP8 rows (fp8 true)
+static int decode_impl(const uint16_t* q_lat, const uint16_t* q_pe, const void* kv_cache, bool fp8,
+                       int num_blocks, int page_size, const int32_t* block_table,
+                       int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
+                       int d_R, int max_seqlen, float softmax_scale, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* part_out,
+                       mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                       void* out_latent, mla_dtype out_dtype, float* lse, void* stream) {
   if (B < 0 || num_blocks < 1 || max_blocks_per_seq < 1 || max_seqlen < 0 || num_splits < 0)
     return MLA_ERR_SHAPE;
   int st = check_heads(T, H);
@@ -228,7 +229,7 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
     p.lse = lse;
     if ((long long)B * n_rg > (1LL << 31) - 8) return MLA_ERR_SHAPE;
     p.n_units = B * n_rg;
-    return launch_status(mla::launch_decode(p, B * n_rg, false, out_dtype == MLA_F32, s));
+    return launch_status(mla::launch_decode(p, B * n_rg, false, out_dtype == MLA_F32, s, false, fp8));
   }
 
   // split mode
@@ -273,12 +274,38 @@ int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
     p.n_items = n_items;
   }
   const bool part_f32 = part_dtype == MLA_F32;
-  if ((st = launch_status(mla::launch_decode(p, max_items * n_rg, true, part_f32, s)))) return st;
+  if ((st = launch_status(mla::launch_decode(p, max_items * n_rg, true, part_f32, s, false, fp8)))) return st;
   if (out_latent) {
     mla::MergeParams mp{part_out, part_lse, split_indptr, B, T * H, out_latent, lse};
     return launch_status(mla::launch_merge(mp, part_f32, out_dtype == MLA_F32, s));
   }
   return MLA_OK;
+}
+
+int mla_decode_latent(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                      int num_blocks, int page_size, const int32_t* block_table,
+                      int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
+                      int d_R, int max_seqlen, float softmax_scale, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* part_out,
+                      mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                      void* out_latent, mla_dtype out_dtype, float* lse, void* stream) {
+  return decode_impl(q_lat, q_pe, kv_cache, false, num_blocks, page_size, block_table, max_blocks_per_seq,
+                     seqlens, B, T, H, r, d_R, max_seqlen, softmax_scale, num_splits, workspace,
+                     workspace_bytes, part_out, part_dtype, part_lse, split_indptr, out_latent, out_dtype, lse,
+                     stream);
+}
+
+int mla_decode_latent_fp8(const uint16_t* q_lat, const uint16_t* q_pe, const uint8_t* kv_cache,
+                          int num_blocks, int page_size, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seqlens, int B, int T, int H, int r,
+                          int d_R, int max_seqlen, float softmax_scale, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* part_out,
+                          mla_dtype part_dtype, float* part_lse, int32_t* split_indptr,
+                          void* out_latent, mla_dtype out_dtype, float* lse, void* stream) {
+  return decode_impl(q_lat, q_pe, kv_cache, true, num_blocks, page_size, block_table, max_blocks_per_seq,
+                     seqlens, B, T, H, r, d_R, max_seqlen, softmax_scale, num_splits, workspace,
+                     workspace_bytes, part_out, part_dtype, part_lse, split_indptr, out_latent, out_dtype, lse,
+                     stream);
 }
 
 int mla_sparse_split_count(int B, int T, int H, int topk, int num_splits, int* splits) {

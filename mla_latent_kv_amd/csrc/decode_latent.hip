@@ -176,6 +176,52 @@ constexpr int dma_part_at(int s) {
 static_assert(kDmaSlot0 + 8 * kDmaStride < kSpIds && kSpIds < kSmPack,
               "sparse ids are read after the step's last load and before the probability writes");
 
+// ---- FP8 cache rows (M5.8 0x0B, "Exact 656-byte FP8 row"): 512 E4M3 codes
+// (byte c = latent column c), four fp32 scales (scale g covers columns
+// [128g, 128g + 128)), 64 bf16 rope values.  The latent is dequantized to bf16
+// (code x scale, rounded to nearest even) into the same tile layout as a bf16
+// row, so the attention itself is unchanged.
+constexpr int kF8Row = 656;
+constexpr int kF8Scales = 512;   // byte offset of the scales in a row
+constexpr int kF8Rope = 528;     // byte offset of the rope values
+// Staging buffer of one step's codes and scales: codes [half][wave parity]
+// [4 load instructions] x 1 KB, then one 256-byte copy of its half's scales
+// per wave.
+constexpr int kStgCodes = 2 * 2 * 4 * 1024;
+constexpr int kStgBytes = kStgCodes + 4 * 256;
+// slots of the six FP8 load instructions of a step (rope of the tile two
+// ahead, then codes and scales of the tile three ahead), the wait for the
+// previous step's loads, and the conversion of the tile two ahead: unit n
+// (one 1 KB code block) is read at kF8Cvt0 + kF8CvtStride n and written out in
+// two halves, 3 and 5 slots later
+constexpr int kF8Wait = 11, kF8Cvt0 = 12, kF8CvtStride = 6;
+constexpr int f8_part_at(int s) { return (s <= 10 && s % 2 == 0) ? s / 2 : -1; }
+// conversion work at slot s: 4 n + phase (0 read unit n, 1 and 2 its two output chunks), or -1
+constexpr int f8_cvt_at(int s) {
+  if (s < kF8Cvt0) return -1;
+  const int x = s - kF8Cvt0, n = x / kF8CvtStride, r = x % kF8CvtStride;
+  if (n >= 4) return -1;
+  return r == 0 ? 4 * n : r == 3 ? 4 * n + 1 : r == 5 ? 4 * n + 2 : -1;
+}
+static_assert(kF8Cvt0 + 3 * kF8CvtStride + 5 < 4 + 40, "conversion stays among the score MFMAs");
+
+// dma16s with the instruction's immediate offset OFF, which moves the global
+// address and the LDS destination alike (so M0 = lds_addr - OFF): one offset
+// register serves several 1 KB blocks of a row group.
+template <int OFF>
+__device__ __forceinline__ void dma16s_imm(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3" ::"v"(voff), "s"(base),
+               "s"(lds_addr - OFF), "n"(OFF)
+               : "memory");
+}
+
+// four E4M3 codes (one dword, code i in byte i) times scale -> four bf16 (two dwords)
+__device__ __forceinline__ u32x2 f8x4_to_bf16(uint32_t codes, float scale) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+  return cvt_bf16x4(f32x4{a[0] * scale, a[1] * scale, b[0] * scale, b[1] * scale});
+}
+
 // Key count of work sequence bb: its length, or in sparse mode the valid
 // prefix of its index row (sequence bb / sp_T's topk_length, at most topk).
 template <bool SPARSE>
@@ -188,10 +234,15 @@ __device__ __forceinline__ int unit_keys(const DecodeParams& p, int bb) {
   }
 }
 
-template <int NB, bool SPLIT, bool OUT_F32, bool SPARSE>
+template <int NB, bool SPLIT, bool OUT_F32, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
-  // step ring; after the last step it is reused to stage the 128 KB output block
-  constexpr int kRingBytes = NB * kStepBytes > 128 * 1024 ? NB * kStepBytes : 128 * 1024;
+  static_assert(!(SPARSE && FP8), "the sparse path reads bf16 rows");
+  static_assert(!FP8 || NB == 3, "FP8 ring: the tiles of steps i, i+1 and the one being converted");
+  constexpr int kRB = FP8 ? kF8Row : kRowBytes;  // bytes per cached row
+  // step ring (FP8: followed by two code staging buffers); after the last step
+  // it is reused to stage the 128 KB output block
+  constexpr int kRingUse = NB * kStepBytes + (FP8 ? 2 * kStgBytes : 0);
+  constexpr int kRingBytes = kRingUse > 128 * 1024 ? kRingUse : 128 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kRingBytes];
   // probabilities of all 128 rows, two steps: [step & 1][kb][row block][lane] x 16 B
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * 2 * 4 * 64 * 16];
@@ -285,6 +336,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   const uint32_t dma_voff = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4) + 64 * (w & 1);
   const int rsw = (l & 15) ^ tile_swz(l >> 4);  // sparse: row of the half this lane loads
   const uint32_t dma_coff = 16 * (l >> 4) + 64 * (w & 1);
+  // FP8 rows, per wave and step: the rope values of its half's 16 rows straight
+  // into the tile (lane l: rope chunk 4 pw + (l >> 4) of row (l & 15) ^ g(l >> 4),
+  // i.e. tile chunk 64 + 4 pw + (l >> 4)); four 1 KB code blocks into the
+  // staging buffer (instruction n, lane l: codes 16 cp .. 16 cp + 15 of row
+  // l & 15, cp = 16 pw + 4 n + (l >> 4)); the half's 64 scales (lane l: scale
+  // l & 3 of row l >> 2).
+  const int pw = w & 1;
+  const uint32_t f8_rope_voff = ((l & 15) ^ tile_swz(l >> 4)) * kF8Row + kF8Rope + 64 * pw + 16 * (l >> 4);
+  const uint32_t f8_code_voff = (l & 15) * kF8Row + 256 * pw + 16 * (l >> 4);
+  const uint32_t f8_scale_voff = (l >> 2) * kF8Row + kF8Scales + 4 * (l & 3);
   int pg_base = 0, pg_vec = 0;
   auto load_window = [&](int base) {
     pg_base = base;
@@ -296,7 +357,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // when the half crosses into another page; page_size is a multiple of 16).
   int dma_page = 0, dma_off = 0;
   const uint8_t* dma_row = cache;
-  const uint32_t page_bytes = (uint32_t)P * kRowBytes;
+  const uint32_t page_bytes = (uint32_t)P * kRB;
   auto page_ptr = [&](int page) -> const uint8_t* {
     if (page < pg_base || page >= pg_base + 64) {
       load_window(page);
@@ -348,12 +409,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     asm volatile("" ::"v"(pg_vec));
   }
   auto dma_start = [&]() {
-    if (half_live(0)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRowBytes;
+    if (half_live(0)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRB;
   };
 
   const uint8_t* dma_base = cache;
   const uint8_t* dma_vaddr = cache;  // sparse: this lane's row + dma_coff
   uint32_t dma_dst = 0;
+  const uint32_t stg_lds = tiles_lds + NB * kStepBytes;  // FP8 code staging (two steps)
+  uint32_t f8_scale_dst = 0;
+  const uint8_t* f8_rope_base = cache;  // FP8: rows whose rope values the step loads
+  uint32_t f8_rope_dst = 0;
   // A half past the end of the range (the second half of a short last step,
   // and every load issued past the last step: the pipeline issues NB-1 steps
   // ahead unconditionally) reads rows 0-15 of the cache, which are valid memory
@@ -361,7 +426,12 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // reads a buffer filled past the last step.  This keeps the issue path and
   // the wait counts free of branches.
   auto issue_prep = [&](int it) {
-    dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
+    if constexpr (FP8) {
+      dma_dst = stg_lds + (it & 1) * kStgBytes + hw * 8192 + pw * 4096;
+      f8_scale_dst = stg_lds + (it & 1) * kStgBytes + kStgCodes + w * 256;
+    } else {
+      dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
+    }
     if constexpr (SPARSE) {
       const uint32_t row = half_live(it) ? min((uint32_t)sidx, p.num_rows - 1u) : (uint32_t)rsw;
       dma_vaddr = cache + (uint64_t)row * kRowBytes + dma_coff;
@@ -377,9 +447,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         dma_off -= P;
         ++dma_page;
       }
-      if (half_live(it + 1)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRowBytes;
+      if (half_live(it + 1)) dma_row = page_ptr(dma_page) + (uint32_t)dma_off * kRB;
     } else {
-      dma_row += kStepTok * kRowBytes;
+      dma_row += kStepTok * kRB;
     }
   };
   auto issue_part = [&](auto n_const) {
@@ -387,6 +457,55 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     if constexpr (SPARSE) dma16v<128 * n>(dma_vaddr, dma_dst + 2048 * n);
     else dma16s(dma_voff + 128 * n, dma_base, dma_dst + 2048 * n);
   };
+  // FP8 load instruction n of a step: 0 the rope values (rows f8_rope_base into
+  // the ring), 1-4 the codes and 5 the scales (rows dma_base into staging)
+  auto f8_issue_part = [&](auto n_const) {
+    constexpr int n = decltype(n_const)::value;
+    if constexpr (n == 0) dma16s(f8_rope_voff, f8_rope_base, f8_rope_dst);
+    else if constexpr (n <= 4) dma16s_imm<64 * (n - 1)>(f8_code_voff, dma_base, dma_dst + 1024 * (n - 1));
+    else dma4s(f8_scale_voff, dma_base, f8_scale_dst);
+  };
+  // tile k's rope values come from the rows of the codes prepared last
+  auto f8_rope_prep = [&](int k) {
+    f8_rope_base = dma_base;
+    f8_rope_dst = tiles_lds + (k % NB) * kStepBytes + hw * kTileBytes + (kTileBytes - 2048) + 1024 * pw;
+  };
+  // FP8 conversion of tile k by this wave: unit n turns the 16 codes per lane of
+  // its load instruction n into chunks 2 cp and 2 cp + 1 of row l & 15 (bf16,
+  // times scale 2 pw + (n >> 1) of the row).  Chunk c = 2 cp + e of row t sits
+  // at tile_pos(c, t), with c & 3 = 2 ((l >> 4) & 1) + e.
+  u32x4 f8_raw;
+  float f8_sc;
+  // Lane terms: f8_rl = 16 l for the code reads (16 (l & 15) for the scales);
+  // f8_wl for output chunk 2 cp, and f8_wl ^ 192 for chunk 2 cp + 1 (the row
+  // swizzles of c & 3 = 2a and 2a + 1 differ by 12 for either a).
+  const uint32_t f8_rl = 16 * l;
+  const uint32_t f8_wl = 512 * (l >> 4) + 16 * ((l & 15) ^ tile_swz(2 * ((l >> 4) & 1)));
+  auto f8_read = [&](int k, auto n_const) {
+    constexpr int n = decltype(n_const)::value;
+    const uint32_t sb = stg_lds + (k & 1) * kStgBytes;
+    f8_raw = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(sb + hw * 8192 + pw * 4096 + 1024 * n + f8_rl);
+    f8_sc = *(const __attribute__((address_space(3))) float*)(uintptr_t)(sb + kStgCodes + w * 256 + 4 * (2 * pw + (n >> 1)) +
+                                                                     (f8_rl & 0xF0u));
+  };
+  auto f8_write = [&](int k, auto n_const, auto e_const) {
+    constexpr int n = decltype(n_const)::value, e = decltype(e_const)::value;
+    const u32x2 v0 = f8x4_to_bf16(f8_raw[2 * e], f8_sc), v1 = f8x4_to_bf16(f8_raw[2 * e + 1], f8_sc);
+    const uint32_t lane = e ? (f8_wl ^ 192u) : f8_wl;
+    const uint32_t dst = tiles_lds + (k % NB) * kStepBytes + hw * kTileBytes + 512 * (16 * pw + 4 * n) + 256 * e + lane;
+    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)dst = u32x4{v0[0], v0[1], v1[0], v1[1]};
+  };
+  auto f8_convert = [&](int k) {  // the whole tile, not interleaved (prologue)
+    static_for<0, 4>([&](auto n) {
+      f8_read(k, n);
+      f8_write(k, n, std::integral_constant<int, 0>{});
+      f8_write(k, n, std::integral_constant<int, 1>{});
+    });
+  };
+  auto f8_issue_codes = [&]() {
+    static_for<1, 6>([&](auto n) { f8_issue_part(n); });
+  };
+
   // sparse: during step i, the ids of step i + NB (entries j0 + 32 (i + NB) +
   // (l & 31)) go to this wave's quarter of probability buffer (i + 1) & 1,
   // which no wave touches between the barrier of step i and this wave's own
@@ -580,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     if (g0 < TH) lim_lo = min(L - T + g0 / H + 1, j1);
   }
 
-  constexpr int PF = 4;   // K operand reads in flight
+  constexpr int PF = FP8 ? 2 : 4;   // K operand reads in flight (FP8: registers for the conversion)
 
   // At most one replay: after a flagged pass every row's reference is within
   // kLazy of its true maximum, so the replay cannot flag again.
@@ -615,6 +734,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         issue(it);
       }
       sidx = sidx_pro[NB - 1];
+    } else if constexpr (FP8) {
+      // tiles 0 and 1: codes, scales and rope values
+      for (int it = 0; it < 2; ++it) {
+        issue_prep(it);
+        f8_rope_prep(it);
+        f8_issue_part(std::integral_constant<int, 0>{});
+        f8_issue_codes();
+      }
     } else {
       for (int it = 0; it < NB - 1; ++it) issue(it);
     }
@@ -630,7 +757,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     bf16x8 pp[3];  // probability operands of row blocks w+1 .. w+3
     {
       // prologue: step 0 landed; its scores and probabilities, first V operands
-      wait_vm<9 * (NB - 2)>();
+      if constexpr (FP8) {
+        // tiles 0 and 1 converted; tile 2's codes requested once the staging
+        // reads of tile 0 are done
+        wait_vm0();
+        f8_convert(0);
+        f8_convert(1);
+        wait_lgkm0();
+        issue_prep(2);
+        f8_issue_codes();
+      } else {
+        wait_vm<9 * (NB - 2)>();
+      }
       barrier();
       if (nsteps == 1 && j1 - j0 < kStepTok) {
         clear_tail(0);
@@ -646,9 +784,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       for (int cb = 0; cb < 4; ++cb) vc[cb] = v_read(vb, 0, cb);
     }
 
-    // body of step i (this wave's loads of step i+NB-1 are issued in it)
+    // body of step i (this wave's loads of step i+NB-1 are issued in it; FP8:
+    // the rope values of tile i+2 and the codes of tile i+3, and tile i+2 is
+    // converted)
     auto step = [&](int i) {
-      issue_prep(i + NB - 1);
+      if constexpr (FP8) {
+        f8_rope_prep(i + 2);
+        issue_prep(i + 3);
+      } else {
+        issue_prep(i + NB - 1);
+      }
       if constexpr (SPARSE) idx_dma(i);
       const bool full = j0 + kStepTok * (i + 2) <= lim_lo;  // step i+1 needs no mask
       // K of step i+1 (after the last step: a resident stale buffer, whose
@@ -687,7 +832,20 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
             else vc[cb] = v_read(vb_next, 0, cb);
           }
         }
-        if constexpr (dma_part_at(s) >= 0) issue_part(std::integral_constant<int, dma_part_at(s)>{});
+        if constexpr (FP8) {
+          if constexpr (f8_part_at(s) >= 0) f8_issue_part(std::integral_constant<int, f8_part_at(s)>{});
+          // the previous step's loads (codes of tile i+2) have landed once at most
+          // this step's six are in flight
+          if constexpr (s == kF8Wait) wait_vm<6>();
+          constexpr int cv = f8_cvt_at(s);
+          if constexpr (cv >= 0) {
+            constexpr int n = cv >> 2, ph = cv & 3;
+            if constexpr (ph == 0) f8_read(i + 2, std::integral_constant<int, n>{});
+            else f8_write(i + 2, std::integral_constant<int, n>{}, std::integral_constant<int, ph - 1>{});
+          }
+        } else if constexpr (dma_part_at(s) >= 0) {
+          issue_part(std::integral_constant<int, dma_part_at(s)>{});
+        }
         if constexpr (SPARSE && s == kSpIds) {
           // the ids of step i + NB have landed once at most the nine tile loads
           // issued after them are in flight
@@ -717,7 +875,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
     for (int i = 0; i < nsteps; ++i) {
       // step i+1 must have landed; the NB-3 later steps may stay in flight
-      wait_vm<9 * (NB - 3)>();
+      // (FP8: the rope values of tile i+1 have landed, the five code and scale
+      // loads issued after them may stay in flight)
+      wait_vm<FP8 ? 5 : 9 * (NB - 3)>();
       // this wave's probability writes are done; the last two V operand reads
       // (two LDS reads each) may stay in flight
       wait_lgkm<4>();
@@ -955,16 +1115,25 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
   }
 }
 
-template <int NB, bool SPLIT, bool F32, bool SPARSE>
+template <int NB, bool SPLIT, bool F32, bool SPARSE, bool FP8 = false>
 static hipError_t launch_decode_t(const DecodeParams& prm, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<NB, SPLIT, F32, SPARSE>), dim3(grid), dim3(256), 0, st, prm);
+  hipLaunchKernelGGL((decode_kernel<NB, SPLIT, F32, SPARSE, FP8>), dim3(grid), dim3(256), 0, st, prm);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeParams& prm, int max_units, bool split, bool out_f32,
-                         hipStream_t st, bool sparse) {
+                         hipStream_t st, bool sparse, bool fp8) {
   constexpr int NB = 4;
   const int grid = ((max_units + 7) / 8) * 8;  // whole XCD rounds; extra workgroups exit
+  if (fp8) {
+    if (sparse) return hipErrorInvalidValue;
+    if (split) {
+      if (out_f32) return launch_decode_t<3, true, true, false, true>(prm, grid, st);
+      return launch_decode_t<3, true, false, false, true>(prm, grid, st);
+    }
+    if (out_f32) return launch_decode_t<3, false, true, false, true>(prm, grid, st);
+    return launch_decode_t<3, false, false, false, true>(prm, grid, st);
+  }
   if (sparse) {
     if (split) {
       if (out_f32) return launch_decode_t<NB, true, true, true>(prm, grid, st);

@@ -9,7 +9,7 @@ namespace mla {
 struct DecodeParams {
   const uint16_t* q_lat;       // [B,T,H,512] bf16
   const uint16_t* q_pe;        // [B,T,H,64] bf16
-  const uint16_t* cache;       // [num_blocks,P,576] bf16
+  const void* cache;           // [num_blocks,P,576] bf16 rows, or [num_blocks,P,656] FP8 rows
   const int32_t* block_table;  // [B,max_blocks]
   const int32_t* seqlens;      // [B]
   const int32_t* work;         // automatic split: [n][4] = (b, j0, j1, slot); NULL = uniform
@@ -94,7 +94,7 @@ struct NormalParams {
 
 // max_units: upper bound of work items x n_rg (the grid is derived from it)
 hipError_t launch_decode(const DecodeParams& p, int max_units, bool split, bool out_f32, hipStream_t st,
-                         bool sparse = false);
+                         bool sparse = false, bool fp8 = false);
 hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipStream_t st);
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);

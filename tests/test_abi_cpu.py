@@ -2,6 +2,7 @@
 include/mla_latent.h declares, and rejects bad host-side arguments before any
 launch (the pointers passed here are never dereferenced)."""
 import ctypes
+import functools
 import os
 import re
 
@@ -69,18 +70,21 @@ def test_unabsorb_validation(lib):
     assert f(None, 0, None, None, 0, 1, 128, 512, 128, None) == OK
 
 
-def _decode(lib, **kw):
+def _decode_any(lib, fp8=False, **kw):
     a = dict(q_lat=P16, q_pe=P16, kv=P16, nb=64, P=64, bt=P16, mb=64, sl=P16, B=2, T=1, H=128,
              r=512, dr=64, maxL=4096, scale=0.07, S=1, ws=None, wsb=0, po=None, pdt=1, pl=None,
              si=None, out=P16, odt=0, lse=None)
     a.update(kw)
-    return lib.mla_decode_latent(a["q_lat"], a["q_pe"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"],
-                                 a["sl"], a["B"], a["T"], a["H"], a["r"], a["dr"], a["maxL"],
-                                 ctypes.c_float(a["scale"]), a["S"], a["ws"], a["wsb"], a["po"],
-                                 a["pdt"], a["pl"], a["si"], a["out"], a["odt"], a["lse"], None)
+    f = lib.mla_decode_latent_fp8 if fp8 else lib.mla_decode_latent
+    return f(a["q_lat"], a["q_pe"], a["kv"], a["nb"], a["P"], a["bt"], a["mb"],
+             a["sl"], a["B"], a["T"], a["H"], a["r"], a["dr"], a["maxL"],
+             ctypes.c_float(a["scale"]), a["S"], a["ws"], a["wsb"], a["po"],
+             a["pdt"], a["pl"], a["si"], a["out"], a["odt"], a["lse"], None)
 
 
-def test_decode_validation(lib):
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_validation(lib, fp8):
+    _decode = functools.partial(_decode_any, fp8=fp8)
     assert _decode(lib, r=256) == UNSUP
     assert _decode(lib, dr=32) == UNSUP
     assert _decode(lib, P=24) == UNSUP          # not a multiple of 16
@@ -134,7 +138,8 @@ def test_merge_validation(lib):
 
 
 def test_binding_names_match_abi():
-    for n in ("mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache",
+    for n in ("mla_absorb_q", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
+              "mla_unabsorb_out", "mla_append_cache",
               "mla_decode_sparse", "mla_sparse_split_count", "mla_decode_normal", "mla_normal_workspace_size",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
         assert callable(getattr(mk, n))
