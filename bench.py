@@ -150,6 +150,67 @@ def bench_sparse(name, K, W, R, dev):
     }
 
 
+def bench_fp8(name, S, K, W, R, dev):
+    """Time the decode kernel over FP8 rows on its workload (S uniform splits,
+    bf16 partials, as the bf16 headline): HIP events around each launch on its
+    stream, cache replicas rotating."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    f = synth.make_fp8_case(synth.FP8_WORKLOADS[name], poison=False)
+    case = f.case
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv0 = torch.from_numpy(f.kv_fp8).to(dev)
+    kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    q_lat = bf16(synth.normal_bf16(case.q_nope.shape[:3] + (512,), 9300, std=0.5))
+    q_pe = bf16(case.q_pe)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seqlens).to(dev)
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, dev,
+                           part_dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    scale = mk.softmax_scale()
+
+    def run(r, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mk.mla_decode_latent_fp8(q_lat, q_pe, kv[r], bt, sl, case.max_seqlen, scale, num_splits=S,
+                                 buffers=buf, merge=False)
+        if ev is not None:
+            ev[1].record(stream)
+        mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, case.B)
+
+    for i in range(W):
+        run(i % R)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        run(i % R, evs[i])
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    us = float(np.mean(ms)) * 1e3
+    bf16_bytes, flops = decode_algorithmic(case)
+    rows = int(np.sum(case.seqlens))
+    nbytes = bf16_bytes - rows * ROW_BYTES + rows * synth.FP8_ROW_BYTES
+    del kv, kv0
+    torch.cuda.empty_cache()
+    return {
+        "fp8_workload": name, "fp8_splits": S,
+        "fp8_decode_us": us,
+        "fp8_decode_us_median": float(np.median(ms)) * 1e3,
+        "fp8_alg_bytes": nbytes,
+        "fp8_GBps": nbytes / (us * 1e-6) / 1e9,
+        "fp8_hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "fp8_tflops": flops / (us * 1e-6) / 1e12,
+        "fp8_mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "fp8_tokens_per_s": case.B * case.T / (us * 1e-6),
+    }
+
+
 def crossover(Ts, S_ctx, B, K, W, dev):
     """Time the absorbed chain (absorb, latent attention with automatic splits,
     merge, un-absorb) and the Normal path (gather, up-projection GEMMs, MHA
@@ -276,6 +337,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-pairs", type=int, default=640)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the decode over FP8 rows (detail fields fp8_*)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the chain with eager launches instead of replaying a captured HIP graph")
     ap.add_argument("--no-sparse", action="store_true",
@@ -510,6 +573,8 @@ def main():
     }
     if not args.no_sparse:
         result["detail"].update(bench_sparse("v3_sparse_b64_topk2048", K, args.warmup, R, dev))
+    if not args.no_fp8:
+        result["detail"].update(bench_fp8("v3_fp8_b64_l4096", 4, K, args.warmup, R, dev))
     if not args.no_cpu:
         try:
             threads = min(16, len(os.sched_getaffinity(0)))

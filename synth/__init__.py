@@ -414,6 +414,11 @@ def make_sparse(wl: Workload, topk: int, valid: Optional[tuple] = None, poison: 
 #     bytes [512, 528)  scale g (little-endian fp32) of columns [128 g, 128 g + 128)
 #     bytes [528, 656)  the 64 rope values (bf16)
 FP8_ROW_BYTES = 656
+# The headline decode geometry (B = 64, 4096-token contexts, 128 heads, page 64)
+# over FP8 rows.
+FP8_WORKLOADS = {
+    "v3_fp8_b64_l4096": Workload("v3_fp8_b64_l4096", B=64, T=1, H=128, L=4096, page_size=64, seed=1007),
+}
 FP8_NAN_CODE = np.uint8(0x7F)   # E4M3FN: exponent and mantissa all ones
 F32_NAN_BITS = np.uint32(0x7FC00000)
 
