@@ -198,8 +198,19 @@ def bench_fp8(name, S, K, W, R, dev):
     nbytes = bf16_bytes - rows * ROW_BYTES + rows * synth.FP8_ROW_BYTES
     del kv, kv0
     torch.cuda.empty_cache()
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "decode_fp8_hbm_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            from mla_latent_kv_amd import _build
+            rec = json.load(open(tpath))
+            if rec.get("source_sha256") == _build.kernel_source_hash() and rec.get("workload") == name \
+                    and int(rec.get("splits", -1)) == S:
+                traffic = rec["bytes_per_launch"]
+        except Exception:
+            traffic = None
     return {
-        "fp8_workload": name, "fp8_splits": S,
+        "fp8_workload": name, "fp8_splits": S, "fp8_traffic": traffic,
         "fp8_decode_us": us,
         "fp8_decode_us_median": float(np.median(ms)) * 1e3,
         "fp8_alg_bytes": nbytes,
