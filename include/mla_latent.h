@@ -48,7 +48,7 @@
  *    the compute entry points: an out-of-range entry is undefined behaviour.
  *    mla_validate_inputs checks it (synchronously) for callers that need that.
  *
- * Fixed geometry of this build: kv_lora_rank r = 512, rope width d_R = 64,
+ * Fixed geometry of this library: kv_lora_rank r = 512, rope width d_R = 64,
  * d_nope = d_V = 128.  H (query heads) is 1..128, T (query tokens per
  * sequence: 1 for plain decode, a few for multi-token decode, up to a
  * prefill-sized block when comparing with the Normal path) is 1..1024,
@@ -69,7 +69,7 @@ typedef enum {
   MLA_ERR_NULL = -1,          /* a required pointer is NULL */
   MLA_ERR_ALIGN = -2,         /* a pointer is not 16-byte aligned */
   MLA_ERR_SHAPE = -3,         /* a size is out of range or sizes disagree */
-  MLA_ERR_UNSUPPORTED = -4,   /* geometry outside what this build implements */
+  MLA_ERR_UNSUPPORTED = -4,   /* geometry outside what this library implements */
   MLA_ERR_WORKSPACE = -5,     /* workspace or partial buffers too small / missing */
   MLA_ERR_LAUNCH = -6,        /* a kernel launch failed */
   MLA_ERR_INVALID_INDEX = -7, /* (mla_validate_inputs) bad block-table entry or length */

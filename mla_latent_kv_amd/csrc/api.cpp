@@ -110,7 +110,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_NULL: return "required pointer is NULL";
     case MLA_ERR_ALIGN: return "pointer not 16-byte aligned (4-byte for int32 arrays)";
     case MLA_ERR_SHAPE: return "size out of range or inconsistent";
-    case MLA_ERR_UNSUPPORTED: return "geometry not supported by this build";
+    case MLA_ERR_UNSUPPORTED: return "geometry not supported by this library";
     case MLA_ERR_WORKSPACE: return "workspace or partial-state buffers missing or too small";
     case MLA_ERR_LAUNCH: return "kernel launch failed";
     case MLA_ERR_INVALID_INDEX: return "block table entry or sequence length out of range";

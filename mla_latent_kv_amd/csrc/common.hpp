@@ -6,7 +6,7 @@
 
 namespace mla {
 
-// Geometry fixed by this build ("MLA in full detail", shapes table: kv_lora_rank 512,
+// Geometry fixed by this library ("MLA in full detail", shapes table: kv_lora_rank 512,
 // rope 64, nope 128, v_head 128).
 constexpr int kR = 512;                 // latent width
 constexpr int kDR = 64;                 // rope width

@@ -59,3 +59,31 @@ def test_contiguous_tiny_workload():
     assert case.kv_cache.shape == (1, 256, 576)
     assert case.block_table.tolist() == [[0]]
     assert case.q_nope.shape == (1, 1, 16, 128)
+
+
+def test_fp8_rows_layout_and_poison():
+    """FP8 rows: 656 bytes; codes never NaN in readable rows, NaN codes and
+    scales in every other row; the rope bytes are make_case's bf16 rope
+    columns; same seed, same bytes; scales in [2^-10, 2^-6]."""
+    wl = synth.scaled(synth.WORKLOADS["v3_ragged_b128"], B=3, ragged=None, lengths=(5, 64, 150), seed=77)
+    f = synth.make_fp8_case(wl)
+    g = synth.make_fp8_case(wl)
+    assert np.array_equal(f.kv_fp8, g.kv_fp8)
+    c = f.case
+    assert f.kv_fp8.shape == c.kv_cache.shape[:2] + (656,) and f.kv_fp8.dtype == np.uint8
+    readable = np.zeros(c.kv_cache.shape[:2], dtype=bool)
+    for b in range(c.B):
+        for j in range(int(c.seqlens[b])):
+            readable[c.block_table[b, j // c.page_size], j % c.page_size] = True
+    codes = f.kv_fp8[..., :512]
+    nan_code = (codes & 0x7F) == 0x7F
+    assert not nan_code[readable].any() and nan_code[~readable].all()
+    sc = np.ascontiguousarray(f.kv_fp8[..., 512:528]).view("<f4")
+    assert np.isnan(sc[~readable]).all()
+    live = sc[readable]
+    assert (live >= 2.0 ** -10).all() and (live <= 2.0 ** -6).all()
+    rope = np.ascontiguousarray(f.kv_fp8[..., 528:]).view("<u2")
+    assert np.array_equal(rope, c.kv_cache[..., 512:])
+    # magnitude codes centred near 108 (the value 96), both signs
+    mag = (codes[readable] & 0x7F).astype(np.float64)
+    assert abs(mag.mean() - 108) < 1.0 and 0.45 < (codes[readable] >> 7).mean() < 0.55
