@@ -46,6 +46,11 @@
 //    few (68 MFMAs, about 60 LDS, 160 vector and 60 scalar instructions per
 //    32 tokens).
 //
+// Variants (template flags): split partials or the final result, fp32 or bf16
+// output, sparse index rows in place of the block table (M5.8 0x0B), and FP8
+// rows (656 bytes, M5.8 0x0B) whose latent codes each wave dequantizes into
+// the bf16 tile layout below, so that everything downstream is shared.
+//
 // LDS layout of a 16-row half (chunk-major): the 16-byte chunk c (c < 72) of
 // row t is stored at chunk position 16c + (t ^ g(c & 3)), g = (0, 12, 8, 4).
 // The K reads (32 rows x 2 chunks) and the transposing V reads are then both
