@@ -45,6 +45,7 @@ CASES = {
     "b300_tiny_h4": synth.scaled(W["v3_b64_l4096"], B=300, H=4, lengths=tuple(1 + (7 * i) % 40 for i in range(300)),
                                  seed=2611),
     "t1024_h1": synth.scaled(W["v3_mtp_b32_t4_h32"], B=1, T=1024, H=1, lengths=(1100,), seed=2612),
+    "t8_h16_p16": synth.scaled(W["v3_mtp_b32_t4_h32"], B=2, T=8, H=16, page_size=16, lengths=(8, 300), seed=2613),
 }
 
 
@@ -185,6 +186,31 @@ def test_fp8_full_headline_sampled(mk):
     buf = mk.DecodeBuffers(c.B, c.T, c.H, c.max_seqlen, c.page_size, 4, "cuda:0", part_dtype=torch.bfloat16)
     lat, lse = mk.mla_decode_latent_fp8(q_lat, d["q_pe"], kv, d["block_table"], d["seqlens"], c.max_seqlen,
                                         SCALE, num_splits=4, buffers=buf)
+    torch.cuda.synchronize()
+    bc = oracle.fp8_case_as_bf16(f)
+    ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits), pairs=pairs)
+    got = to_f64(lat)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    for b, h in pairs:
+        assert_close(got[b, :, h], ref_lat[b, :, h], f"latent b={b} h={h}")
+        assert_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
+
+
+def test_fp8_full_long_context_sampled(mk):
+    """The 4 x 131072 long-context workload over FP8 rows with its 64 uniform
+    splits (256 work units) and the merge, on sampled pairs."""
+    import torch
+    log("[fp8 full] v3_long_b4_l131072 (sampled pairs)")
+    f = synth.make_fp8_case(W["v3_long_b4_l131072"])
+    c = f.case
+    pairs = sample_pairs(c.B, c.H, 6, 2630)
+    d = upload(c)
+    kv = torch.from_numpy(f.kv_fp8).to("cuda:0")
+    ql_bits = synth.normal_bf16(c.q_nope.shape[:3] + (512,), 9210, std=0.5)
+    q_lat = bf16_tensor(ql_bits, "cuda:0")
+    buf = mk.DecodeBuffers(c.B, c.T, c.H, c.max_seqlen, c.page_size, 64, "cuda:0", part_dtype=torch.bfloat16)
+    lat, lse = mk.mla_decode_latent_fp8(q_lat, d["q_pe"], kv, d["block_table"], d["seqlens"], c.max_seqlen,
+                                        SCALE, num_splits=64, buffers=buf, out_dtype=torch.float32)
     torch.cuda.synchronize()
     bc = oracle.fp8_case_as_bf16(f)
     ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits), pairs=pairs)
