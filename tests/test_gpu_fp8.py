@@ -219,3 +219,54 @@ def test_fp8_full_long_context_sampled(mk):
     for b, h in pairs:
         assert_close(got[b, :, h], ref_lat[b, :, h], f"latent b={b} h={h}")
         assert_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 0])
+@pytest.mark.parametrize("hot_token", [3, 137, 290])
+def test_fp8_score_growth_past_reference(mk, S, hot_token):
+    """One FP8 row whose dequantized latent is 448 x scale x sign(q~[0,0,0,:])
+    (scale chosen so its entries are 16 times the query's mean magnitude):
+    head 0's score there exceeds every earlier one by far more than the
+    kernel's tolerated growth, so the work unit is replayed with a raised
+    reference -- the FP8 prologue then runs a second time.  The result must
+    match the oracle, and head 0 of sequence 0 must return that row."""
+    import torch
+    log(f"[fp8 growth] hot key at {hot_token}, num_splits={S}")
+    f = synth.make_fp8_case(CASES["v3_b3_l300"])
+    ql_bits = synth.normal_bf16(f.case.q_nope.shape[:3] + (512,), 9400 + hot_token, std=0.5)
+    q0 = bits_to_f64(ql_bits[0, 0, 0, :])
+    P = f.case.page_size
+    blk, off = int(f.case.block_table[0, hot_token // P]), hot_token % P
+    f.kv_fp8[blk, off, :512] = np.where(q0 < 0, 0xFE, 0x7E).astype(np.uint8)      # -448 / +448
+    scale = np.float32(16.0 * np.mean(np.abs(q0)) / 448.0)
+    f.kv_fp8[blk, off, 512:528] = np.full(4, scale, dtype="<f4").view(np.uint8)
+    bc = oracle.fp8_case_as_bf16(f)
+    d = upload(f.case)
+    kv = torch.from_numpy(f.kv_fp8).to("cuda:0")
+    lat, lse = mk.mla_decode_latent_fp8(bf16_tensor(ql_bits, "cuda:0"), d["q_pe"], kv, d["block_table"],
+                                        d["seqlens"], bc.max_seqlen, SCALE, num_splits=S, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
+    hot = bits_to_f64(bc.kv_cache[blk, off, :512])
+    assert float(np.max(np.abs(ref_lat[0, 0, 0] - hot))) < 1e-6 * float(np.max(np.abs(hot)))
+    assert_close(to_f64(lat), ref_lat, "latent")
+    assert_close(to_f64(lse), ref_lse, "lse")
+
+
+def test_fp8_auto_split_full_chip_runs_unsplit(mk):
+    """Automatic splits with an output wanted and one work unit per sequence
+    already reaching the CU count (300 sequences): the call runs unsplit and
+    leaves the partial buffers untouched."""
+    import torch
+    log("[fp8 split auto, full chip] b300_tiny_h4")
+    f, bc, d, ql_bits = _prep("b300_tiny_h4")
+    buf = mk.DecodeBuffers(bc.B, bc.T, bc.H, bc.max_seqlen, bc.page_size, 0, "cuda:0")
+    buf.part_lse.fill_(123.0)
+    lat, lse = mk.mla_decode_latent_fp8(bf16_tensor(ql_bits, "cuda:0"), d["q_pe"], d["kv_fp8"], d["block_table"],
+                                        d["seqlens"], bc.max_seqlen, SCALE, num_splits=0, out_dtype=torch.float32,
+                                        buffers=buf)
+    torch.cuda.synchronize()
+    assert bool((buf.part_lse == 123.0).all())
+    ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
+    assert_close(to_f64(lat), ref_lat, "latent")
+    assert_close(to_f64(lse), ref_lse, "lse")
