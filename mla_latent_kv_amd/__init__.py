@@ -180,7 +180,10 @@ def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softma
     dr = q_pe.shape[3]
     num_blocks, page_size, _ = kv_cache.shape
     max_blocks = block_table.shape[1]
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype is None:
+        out_dtype = out_latent.dtype if out_latent is not None else torch.bfloat16
+    elif out_latent is not None and out_latent.dtype != out_dtype:
+        raise ValueError("out_latent's dtype differs from out_dtype")
     want_out = num_splits == 1 or merge
     if want_out and out_latent is None:
         out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
@@ -285,7 +288,10 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     topk = indices.shape[2]
     if tuple(indices.shape[:2]) != (B, T) or (topk_length is not None and topk_length.shape[0] < B):
         raise ValueError("mla_decode_sparse: indices / topk_length do not match q_lat")
-    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype is None:
+        out_dtype = out_latent.dtype if out_latent is not None else torch.bfloat16
+    elif out_latent is not None and out_latent.dtype != out_dtype:
+        raise ValueError("out_latent's dtype differs from out_dtype")
     if buffers is None:
         buffers = SparseBuffers(B, T, H, topk, num_splits, q_lat.device)
     S = buffers.num_splits

@@ -246,3 +246,17 @@ def test_normal_workspace_size(lib):
     assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 1024, ctypes.byref(nb)) == OK
     assert nb.value == one // 4 + 4 * 128 * 128 * 4 + 2 * (4 * 128 * 4)   # + output, max and sum state
     assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 1024, None) == NULL
+
+
+def test_binding_takes_the_output_dtype_from_out_latent():
+    """A caller-provided out_latent fixes the output dtype; a conflicting
+    out_dtype is rejected before any call (CPU tensors: nothing is launched)."""
+    import torch
+    q = torch.zeros((1, 1, 1, 512), dtype=torch.bfloat16)
+    qp = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    out = torch.zeros((1, 1, 1, 512), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(q, qp, kv, bt, sl, 1, 0.07, out_latent=out, out_dtype=torch.bfloat16)

@@ -270,3 +270,75 @@ def test_fp8_auto_split_full_chip_runs_unsplit(mk):
     ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
     assert_close(to_f64(lse), ref_lse, "lse")
+
+
+def test_fp8_page_placement_is_bitwise_invisible(mk):
+    """The same logical FP8 rows laid out in (sequence, page) order instead of
+    the seeded permutation give bit-identical results."""
+    import torch
+    log("[fp8 bitwise] permuted vs identity pages")
+    f, bc, d, ql_bits = _prep("v3_ragged_b5")
+    c = f.case
+    P = c.page_size
+    pages = [(int(L) + P - 1) // P for L in c.seqlens]
+    rows = np.empty((sum(pages), P, 656), dtype=np.uint8)
+    table = np.full_like(c.block_table, -1)
+    k = 0
+    for b in range(c.B):
+        for pg in range(pages[b]):
+            rows[k] = f.kv_fp8[c.block_table[b, pg]]
+            table[b, pg] = k
+            k += 1
+    ql = bf16_tensor(ql_bits, "cuda:0")
+    outs = []
+    for kv, bt in ((f.kv_fp8, c.block_table), (rows, table)):
+        lat, lse = mk.mla_decode_latent_fp8(ql, d["q_pe"], torch.from_numpy(kv).to("cuda:0"),
+                                            torch.from_numpy(bt).to("cuda:0"), d["seqlens"], bc.max_seqlen,
+                                            SCALE, out_dtype=torch.float32)
+        outs.append((lat.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("S", [1, 4, 0])
+def test_fp8_graph_replays_match_eager(mk, S):
+    """The FP8 decode (and its merge) captured in a HIP graph: every replay,
+    with eager work overwriting the outputs in between, equals the eager
+    result bit for bit."""
+    import torch
+    log(f"[fp8 graph] num_splits={S}")
+    f, bc, d, ql_bits = _prep("mtp_t4_h32")
+    B, T, H = bc.B, bc.T, bc.H
+    dev = "cuda:0"
+    q_lat = bf16_tensor(ql_bits, dev)
+    buf = mk.DecodeBuffers(B, T, H, bc.max_seqlen, bc.page_size, S, dev, part_dtype=torch.bfloat16) \
+        if S != 1 else None
+    latent = torch.empty((B, T, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+
+    def step():
+        if S == 1:
+            mk.mla_decode_latent_fp8(q_lat, d["q_pe"], d["kv_fp8"], d["block_table"], d["seqlens"], bc.max_seqlen,
+                                     SCALE, num_splits=1, out_latent=latent, lse=lse)
+        else:
+            mk.mla_decode_latent_fp8(q_lat, d["q_pe"], d["kv_fp8"], d["block_table"], d["seqlens"], bc.max_seqlen,
+                                     SCALE, num_splits=S, buffers=buf, merge=False)
+            mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, B, out_latent=latent, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (latent.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        latent.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(latent, ref[0]) and torch.equal(lse, ref[1]), f"replay {rep} differs from eager"
