@@ -91,7 +91,18 @@ def _torch():
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor the C ABI reads as dense row-major memory."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MLA library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtypes, what):
+    """Reject a tensor whose element type the C ABI would misread."""
+    if t is not None and t.dtype not in dtypes:
+        raise ValueError(f"{what}: expected {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
 
 
 def _stream(stream):
@@ -117,6 +128,8 @@ def _dtype_code(dtype) -> int:
 def mla_absorb_q(q_nope, w_uk, q_lat=None, stream=None):
     """q_nope [B,T,H,128] bf16, w_uk [H,128,512] bf16 -> q_lat [B,T,H,512] bf16."""
     torch = _torch()
+    for t, n in ((q_nope, "q_nope"), (w_uk, "w_uk"), (q_lat, "q_lat")):
+        _need(t, (torch.bfloat16,), "mla_absorb_q " + n)
     B, T, H, dn = q_nope.shape
     r = w_uk.shape[2]
     if q_lat is None:
@@ -176,6 +189,13 @@ def mla_decode_latent_fp8(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqle
 def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
             num_splits, out_dtype, buffers, out_latent, lse, merge, stream):
     torch = _torch()
+    what = "mla_decode_latent_fp8" if fp8 else "mla_decode_latent"
+    _need(q_lat, (torch.bfloat16,), what + " q_lat")
+    _need(q_pe, (torch.bfloat16,), what + " q_pe")
+    _need(kv_cache, (torch.uint8,) if fp8 else (torch.bfloat16,), what + " kv_cache")
+    _need(block_table, (torch.int32,), what + " block_table")
+    _need(seqlens, (torch.int32,), what + " seqlens")
+    _need(lse, (torch.float32,), what + " lse")
     B, T, H, r = q_lat.shape
     dr = q_pe.shape[3]
     num_blocks, page_size, _ = kv_cache.shape
@@ -211,6 +231,9 @@ def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=N
                      out_dtype=None, stream=None):
     """Merge partials -> (out_latent [B,T,H,512], lse [B,T,H])."""
     torch = _torch()
+    _need(part_lse, (torch.float32,), "mla_merge_splits part_lse")
+    _need(split_indptr, (torch.int32,), "mla_merge_splits split_indptr")
+    _need(lse, (torch.float32,), "mla_merge_splits lse")
     _, T, H, r = part_out.shape
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     if out_latent is None:
@@ -227,6 +250,9 @@ def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=N
 def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
     """latent [B,T,H,512] bf16/f32, w_uv [H,128,512] bf16 -> out [B,T,H,128] f32."""
     torch = _torch()
+    _need(latent, (torch.bfloat16, torch.float32), "mla_unabsorb_out latent")
+    _need(w_uv, (torch.bfloat16,), "mla_unabsorb_out w_uv")
+    _need(out, (torch.float32,), "mla_unabsorb_out out")
     B, T, H, r = latent.shape
     dv = w_uv.shape[1]
     if out is None:
@@ -240,6 +266,11 @@ def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
 def mla_append_cache(c_new, kpe_new, kv_cache, block_table, seqlens, stream=None):
     """Write the T new rows of every sequence at positions seqlens[b]-T+t of the
     paged cache (in place).  c_new [B,T,512] bf16, kpe_new [B,T,64] bf16."""
+    torch = _torch()
+    for t, n in ((c_new, "c_new"), (kpe_new, "kpe_new"), (kv_cache, "kv_cache")):
+        _need(t, (torch.bfloat16,), "mla_append_cache " + n)
+    _need(block_table, (torch.int32,), "mla_append_cache block_table")
+    _need(seqlens, (torch.int32,), "mla_append_cache seqlens")
     B, T, r = c_new.shape
     dr = kpe_new.shape[2]
     num_blocks, page_size, _ = kv_cache.shape
@@ -282,6 +313,11 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     Returns (out_latent, lse); with more than one split and merge=False the
     partials stay in ``buffers`` and (None, None) is returned."""
     torch = _torch()
+    _need(q_lat, (torch.bfloat16,), "mla_decode_sparse q_lat")
+    _need(q_pe, (torch.bfloat16,), "mla_decode_sparse q_pe")
+    _need(kv_cache, (torch.bfloat16,), "mla_decode_sparse kv_cache")
+    _need(indices, (torch.int32,), "mla_decode_sparse indices")
+    _need(topk_length, (torch.int32,), "mla_decode_sparse topk_length")
     B, T, H, r = q_lat.shape
     dr = q_pe.shape[3]
     num_blocks, page_size, _ = kv_cache.shape
@@ -326,6 +362,10 @@ def mla_decode_normal(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, 
     Returns (out [B,T,H,128] f32, lse [B,T,H] f32).  ``chunk`` defaults to
     max_seqlen (one chunk)."""
     torch = _torch()
+    for t, n in ((q_nope, "q_nope"), (q_pe, "q_pe"), (w_uk, "w_uk"), (w_uv, "w_uv"), (kv_cache, "kv_cache")):
+        _need(t, (torch.bfloat16,), "mla_decode_normal " + n)
+    _need(block_table, (torch.int32,), "mla_decode_normal block_table")
+    _need(seqlens, (torch.int32,), "mla_decode_normal seqlens")
     B, T, H, dn = q_nope.shape
     dr = q_pe.shape[3]
     dv, r = w_uv.shape[1], w_uk.shape[2]

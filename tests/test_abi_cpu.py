@@ -260,3 +260,25 @@ def test_binding_takes_the_output_dtype_from_out_latent():
     out = torch.zeros((1, 1, 1, 512), dtype=torch.float32)
     with pytest.raises(ValueError):
         mk.mla_decode_latent(q, qp, kv, bt, sl, 1, 0.07, out_latent=out, out_dtype=torch.bfloat16)
+
+
+def test_binding_rejects_misread_tensors():
+    """Element types the C ABI would misread, and non-contiguous views, raise
+    in the binding (CPU tensors: nothing is launched)."""
+    import torch
+    q = torch.zeros((1, 1, 1, 512), dtype=torch.bfloat16)
+    qp = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 16, 576), dtype=torch.bfloat16)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(q.float(), qp, kv, bt, sl, 1, 0.07)                 # fp32 query
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(q, qp, kv, bt.long(), sl, 1, 0.07)                  # int64 table
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent_fp8(q, qp, kv, bt, sl, 1, 0.07)                     # bf16 rows to the FP8 entry
+    wide = torch.zeros((1, 1, 1, 1024), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(wide[..., ::2], qp, kv, bt, sl, 1, 0.07)            # strided view
+    with pytest.raises(ValueError):
+        mk.mla_absorb_q(torch.zeros((1, 1, 1, 128)), torch.zeros((1, 128, 512), dtype=torch.bfloat16))
