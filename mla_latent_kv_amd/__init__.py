@@ -99,6 +99,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, shape, what):
+    """Reject a tensor whose shape disagrees with the sizes passed to the C ABI
+    (the kernels index by those sizes)."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _need(t, dtypes, what):
     """Reject a tensor whose element type the C ABI would misread."""
     if t is not None and t.dtype not in dtypes:
@@ -131,6 +138,8 @@ def mla_absorb_q(q_nope, w_uk, q_lat=None, stream=None):
     for t, n in ((q_nope, "q_nope"), (w_uk, "w_uk"), (q_lat, "q_lat")):
         _need(t, (torch.bfloat16,), "mla_absorb_q " + n)
     B, T, H, dn = q_nope.shape
+    _shape(w_uk, (H, dn, w_uk.shape[2]), "mla_absorb_q w_uk")
+    _shape(q_lat, (B, T, H, w_uk.shape[2]), "mla_absorb_q q_lat")
     r = w_uk.shape[2]
     if q_lat is None:
         q_lat = torch.empty((B, T, H, r), dtype=torch.bfloat16, device=q_nope.device)
@@ -200,6 +209,12 @@ def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softma
     dr = q_pe.shape[3]
     num_blocks, page_size, _ = kv_cache.shape
     max_blocks = block_table.shape[1]
+    _shape(q_pe, (B, T, H, dr), what + " q_pe")
+    _shape(kv_cache, (num_blocks, page_size, 656 if fp8 else r + dr), what + " kv_cache")
+    if block_table.dim() != 2 or block_table.shape[0] < B or seqlens.dim() != 1 or seqlens.shape[0] < B:
+        raise ValueError(what + ": block_table [>=B, max_blocks] and seqlens [>=B] expected")
+    _shape(out_latent, (B, T, H, r), what + " out_latent")
+    _shape(lse, (B, T, H), what + " lse")
     if out_dtype is None:
         out_dtype = out_latent.dtype if out_latent is not None else torch.bfloat16
     elif out_latent is not None and out_latent.dtype != out_dtype:
@@ -235,6 +250,10 @@ def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=N
     _need(split_indptr, (torch.int32,), "mla_merge_splits split_indptr")
     _need(lse, (torch.float32,), "mla_merge_splits lse")
     _, T, H, r = part_out.shape
+    _shape(part_lse, (part_out.shape[0], T, H), "mla_merge_splits part_lse")
+    _shape(split_indptr, (B + 1,), "mla_merge_splits split_indptr")
+    _shape(out_latent, (B, T, H, r), "mla_merge_splits out_latent")
+    _shape(lse, (B, T, H), "mla_merge_splits lse")
     out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
     if out_latent is None:
         out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=part_out.device)
@@ -255,6 +274,8 @@ def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
     _need(out, (torch.float32,), "mla_unabsorb_out out")
     B, T, H, r = latent.shape
     dv = w_uv.shape[1]
+    _shape(w_uv, (H, dv, r), "mla_unabsorb_out w_uv")
+    _shape(out, (B, T, H, dv), "mla_unabsorb_out out")
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=latent.device)
     _check(load_library().mla_unabsorb_out(_ptr(latent), _dtype_code(latent.dtype), _ptr(w_uv),
@@ -276,6 +297,7 @@ def mla_append_cache(c_new, kpe_new, kv_cache, block_table, seqlens, stream=None
     num_blocks, page_size, _ = kv_cache.shape
     if tuple(kpe_new.shape[:2]) != (B, T) or seqlens.shape[0] < B or block_table.shape[0] < B:
         raise ValueError("mla_append_cache: c_new, kpe_new, seqlens and block_table disagree on B, T")
+    _shape(kv_cache, (num_blocks, page_size, r + dr), "mla_append_cache kv_cache")
     _check(load_library().mla_append_cache(_ptr(c_new), _ptr(kpe_new), _ptr(kv_cache), num_blocks, page_size,
                                            _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, T, r,
                                            dr, _stream(stream)), "mla_append_cache")
@@ -324,6 +346,10 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     topk = indices.shape[2]
     if tuple(indices.shape[:2]) != (B, T) or (topk_length is not None and topk_length.shape[0] < B):
         raise ValueError("mla_decode_sparse: indices / topk_length do not match q_lat")
+    _shape(q_pe, (B, T, H, dr), "mla_decode_sparse q_pe")
+    _shape(kv_cache, (num_blocks, page_size, r + dr), "mla_decode_sparse kv_cache")
+    _shape(out_latent, (B, T, H, r), "mla_decode_sparse out_latent")
+    _shape(lse, (B, T, H), "mla_decode_sparse lse")
     if out_dtype is None:
         out_dtype = out_latent.dtype if out_latent is not None else torch.bfloat16
     elif out_latent is not None and out_latent.dtype != out_dtype:
@@ -370,6 +396,12 @@ def mla_decode_normal(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, 
     dr = q_pe.shape[3]
     dv, r = w_uv.shape[1], w_uk.shape[2]
     num_blocks, page_size, _ = kv_cache.shape
+    _shape(q_pe, (B, T, H, dr), "mla_decode_normal q_pe")
+    _shape(w_uk, (H, dn, r), "mla_decode_normal w_uk")
+    _shape(w_uv, (H, dv, r), "mla_decode_normal w_uv")
+    _shape(kv_cache, (num_blocks, page_size, r + dr), "mla_decode_normal kv_cache")
+    if block_table.shape[0] < B or seqlens.shape[0] < B:
+        raise ValueError("mla_decode_normal: block_table and seqlens need a row per sequence")
     chunk = int(max_seqlen) if chunk is None else int(chunk)
     need = mla_normal_workspace_size(B, T, H, int(max_seqlen), chunk)
     if workspace is None:

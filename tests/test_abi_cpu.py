@@ -282,3 +282,23 @@ def test_binding_rejects_misread_tensors():
         mk.mla_decode_latent(wide[..., ::2], qp, kv, bt, sl, 1, 0.07)            # strided view
     with pytest.raises(ValueError):
         mk.mla_absorb_q(torch.zeros((1, 1, 1, 128)), torch.zeros((1, 128, 512), dtype=torch.bfloat16))
+
+
+def test_binding_rejects_shape_mismatches():
+    """Sizes the kernels index by must agree across tensors (CPU tensors:
+    nothing is launched)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros((2, 1, 4, 512), dtype=bf)
+    kv = torch.zeros((1, 16, 576), dtype=bf)
+    bt = torch.zeros((2, 1), dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(q, torch.zeros((2, 1, 3, 64), dtype=bf), kv, bt, sl, 1, 0.07)   # q_pe heads
+    with pytest.raises(ValueError):
+        mk.mla_decode_latent(q, torch.zeros((2, 1, 4, 64), dtype=bf), kv, bt[:1], sl, 1, 0.07)  # table rows
+    with pytest.raises(ValueError):
+        mk.mla_unabsorb_out(q, torch.zeros((3, 128, 512), dtype=bf))                           # w_uv heads
+    with pytest.raises(ValueError):
+        mk.mla_absorb_q(torch.zeros((2, 1, 4, 128), dtype=bf), torch.zeros((4, 128, 512), dtype=bf),
+                        q_lat=torch.zeros((2, 1, 4, 256), dtype=bf))
