@@ -94,6 +94,8 @@ def _ptr(t):
     """Device address of a tensor the C ABI reads as dense row-major memory."""
     if t is None:
         return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to the MLA library must be device (HIP) tensors")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the MLA library must be contiguous")
     return ctypes.c_void_p(t.data_ptr())

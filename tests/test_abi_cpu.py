@@ -302,3 +302,11 @@ def test_binding_rejects_shape_mismatches():
     with pytest.raises(ValueError):
         mk.mla_absorb_q(torch.zeros((2, 1, 4, 128), dtype=bf), torch.zeros((4, 128, 512), dtype=bf),
                         q_lat=torch.zeros((2, 1, 4, 256), dtype=bf))
+
+
+def test_binding_rejects_host_tensors():
+    """A host tensor never reaches a kernel (it would be a device memory fault)."""
+    import torch
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="device"):
+        mk.mla_absorb_q(torch.zeros((1, 1, 1, 128), dtype=bf), torch.zeros((1, 128, 512), dtype=bf))
