@@ -291,9 +291,13 @@ def crossover(Ts, S_ctx, B, K, W, dev):
     return rows
 
 
-def cpu_baseline(case, pairs_n, threads, seed=123):
+def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
-    and scale linearly to the whole batch (its cost is linear in pairs x keys)."""
+    and scale linearly to the whole batch (its cost is linear in pairs x keys).
+    With ``gpu_out`` (the timed step's output), the oracle results also check
+    it: the sampled pairs against the Normal path, every element against the
+    absorbed mirror, to the product tolerance -- proof that the timed kernels
+    computed the step."""
     import numpy as np
     import oracle
     rng = np.random.default_rng(seed)
@@ -302,7 +306,7 @@ def cpu_baseline(case, pairs_n, threads, seed=123):
     pairs = np.stack([idx // H, idx % H], axis=1).astype(np.int32)
     oracle.lib()
     t0 = time.perf_counter()
-    oracle.normal_decode(case, pairs=pairs, nthreads=threads)
+    ref_pairs, _ = oracle.normal_decode(case, pairs=pairs, nthreads=threads)
     dt = time.perf_counter() - t0
     keys_sample = float(np.sum(case.seqlens[pairs[:, 0]]))
     keys_all = float(np.sum(case.seqlens)) * H
@@ -311,8 +315,19 @@ def cpu_baseline(case, pairs_n, threads, seed=123):
     t0 = time.perf_counter()
     ql = oracle.absorb(case.q_nope, case.w_uk)
     lat, _ = oracle.latent_attention(case, ql, nthreads=threads)
-    oracle.unabsorb(lat, case.w_uv)
+    ref_all = oracle.unabsorb(lat, case.w_uv)
     t_mirror = time.perf_counter() - t0
+    check = None
+    if gpu_out is not None:
+        sel = (pairs[:, 0], slice(None), pairs[:, 1])
+        got_s, ref_s = gpu_out[sel], ref_pairs[sel]
+        tol_s = 1e-2 * float(np.max(np.abs(ref_s))) + 1e-3
+        err_s = float(np.max(np.abs(got_s - ref_s)))
+        tol_a = 1e-2 * float(np.max(np.abs(ref_all))) + 1e-3
+        err_a = float(np.max(np.abs(gpu_out - ref_all)))
+        check = {"max_abs_err_vs_normal_sample": err_s, "tol_normal_sample": tol_s,
+                 "max_abs_err_vs_absorbed_mirror": err_a, "tol_absorbed_mirror": tol_a,
+                 "pass": bool(np.isfinite(gpu_out).all() and err_s <= tol_s and err_a <= tol_a)}
     cpu = "unknown CPU"
     try:
         for line in open("/proc/cpuinfo"):
@@ -332,6 +347,7 @@ def cpu_baseline(case, pairs_n, threads, seed=123):
         "absorbed_mirror_value": case.B * case.T / t_mirror,
         "absorbed_mirror_sample": f"fp64 absorbed mirror (absorb, latent attention, un-absorb) on the whole "
                                   f"batch: {t_mirror:.1f} s on {threads} threads",
+        "timed_output_check": check,
     }
 
 
@@ -591,7 +607,8 @@ def main():
             threads = min(16, len(os.sched_getaffinity(0)))
         except AttributeError:
             threads = min(16, os.cpu_count() or 1)
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs, threads)
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs, threads,
+                                              gpu_out=out.double().cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
