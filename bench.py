@@ -62,16 +62,17 @@ def chain_algorithmic(case, decode_bytes):
     return decode_bytes + absorb + unabsorb
 
 
-def sparse_algorithmic(sc, n_splits):
-    """Algorithmic bytes and FLOPs of one sparse decode launch (split partials in
-    bf16): every valid selected row once, its index entry, the query, the
-    partial outputs and their lse."""
+def sparse_algorithmic(sc):
+    """Algorithmic bytes and FLOPs of one sparse decode launch, counted as for the
+    dense kernel: every valid selected row once with its index entry, the
+    query, the bf16 latent output and the lse.  Split partials are overhead of
+    the kernel, not useful traffic, so they are not counted."""
     import numpy as np
     B, T, H = sc.B, sc.T, sc.H
     n = sc.topk if sc.topk_length is None else np.minimum(sc.topk_length, sc.topk).astype(np.int64)
     keys = int(np.sum(n)) * T if sc.topk_length is not None else B * T * sc.topk
     q_bytes = B * T * H * (512 + 64) * 2
-    out_bytes = B * T * n_splits * H * (512 * 2 + 4)
+    out_bytes = B * T * H * (512 * 2 + 4)
     nbytes = keys * (ROW_BYTES + 4) + q_bytes + out_bytes
     flops = 2 * H * keys * (576 + 512)
     return nbytes, flops
@@ -123,7 +124,7 @@ def bench_sparse(name, K, W, R, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
-    nbytes, flops = sparse_algorithmic(sc, S)
+    nbytes, flops = sparse_algorithmic(sc)
     del kv, kv0
     torch.cuda.empty_cache()
     traffic = None
@@ -291,6 +292,162 @@ def crossover(Ts, S_ctx, B, K, W, dev):
     return rows
 
 
+class MetricsSampler:
+    """Samples the GPU's firmware metrics table (amdsmi gpu_metrics: gfx clock,
+    socket power, energy counter, throttle flags) from a thread every `period`
+    seconds.  Reading the table does not touch the HIP runtime."""
+
+    def __init__(self, period=0.005):
+        import threading
+        self.period = period
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self.error = None
+
+    def start(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no permission or no library: report, do not fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def _run(self):
+        while not self._stop.is_set():
+            t = time.perf_counter()
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            row = {"t": t}
+            for k, v in m.items():
+                if isinstance(v, (int, float)) and not isinstance(v, bool):
+                    row[k] = v
+                elif isinstance(v, list) and v and all(isinstance(x, (int, float)) for x in v):
+                    vals = [x for x in v if x not in (65535, 0xFFFFFFFF, 0xFFFFFFFFFFFFFFFF)]
+                    if vals:
+                        row[k + "_mean"] = sum(vals) / len(vals)
+            self.samples.append(row)
+            self._stop.wait(self.period)
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        try:
+            self._smi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+    def summary(self, t0, t1, keys):
+        import numpy as np
+        rows = [r for r in self.samples if t0 <= r["t"] <= t1]
+        out = {"samples": len(rows), "error": self.error}
+        for k in keys:
+            vals = [r[k] for r in rows if k in r]
+            if vals:
+                out[k] = {"median": float(np.median(vals)), "min": float(np.min(vals)),
+                          "max": float(np.max(vals))}
+        e = [(r["t"], r["energy_accumulator"]) for r in rows if "energy_accumulator" in r]
+        if len(e) >= 2 and e[-1][0] > e[0][0]:
+            # the accumulator counts in units of 15.259 uJ (firmware convention of this metrics table)
+            out["energy_accumulator_W"] = (e[-1][1] - e[0][1]) * 15.259e-6 / (e[-1][0] - e[0][0])
+        return out
+
+
+def clock_sample(seconds, kind, dev):
+    """Run one decode kernel of the headline geometry back to back for `seconds`
+    (three cache replicas rotating, 4 uniform splits, bf16 partials) while the
+    firmware metrics table is sampled; report the kernel's mean duration (HIP
+    events on its stream), the gfx clock and power during the loop, and the
+    cycles per 32-token step that the two imply."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    if kind == "fp8":
+        f = synth.make_fp8_case(synth.FP8_WORKLOADS["v3_fp8_b64_l4096"], poison=False)
+        case = f.case
+        kv0 = torch.from_numpy(f.kv_fp8).to(dev)
+        fn = mk.mla_decode_latent_fp8
+    else:
+        case = synth.make_case(synth.WORKLOADS[HEADLINE], poison=False)
+        kv0 = torch.from_numpy(np.ascontiguousarray(case.kv_cache).view(np.int16)).view(torch.bfloat16).to(dev)
+        fn = mk.mla_decode_latent
+    kv = [kv0] + [kv0.clone() for _ in range(2)]
+    q_lat = torch.from_numpy(synth.normal_bf16(case.q_nope.shape[:3] + (512,), 9300, std=0.5).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    q_pe = torch.from_numpy(np.ascontiguousarray(case.q_pe).view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seqlens).to(dev)
+    S = 4
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, dev,
+                           part_dtype=torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    scale = mk.softmax_scale()
+
+    def launch(i):
+        fn(q_lat, q_pe, kv[i % 3], bt, sl, case.max_seqlen, scale, num_splits=S, buffers=buf, merge=False)
+
+    for i in range(20):
+        launch(i)
+    torch.cuda.synchronize()
+    sampler = MetricsSampler().start()
+    time.sleep(0.3)
+    idle_t1 = time.perf_counter()
+    batch = 64
+    evs = []
+    n = 0
+    t0 = time.perf_counter()
+    pending = []
+    while time.perf_counter() - t0 < seconds:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            launch(n)
+            n += 1
+        e1.record(stream)
+        evs.append((e0, e1))
+        pending.append(e1)
+        if len(pending) > 2:  # keep about two batches queued
+            pending.pop(0).synchronize()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    time.sleep(0.2)
+    sampler.stop()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs[1:]])) * 1e3 / batch
+    keys = ["current_gfxclk", "average_gfxclk_frequency", "current_gfxclks_mean", "current_socket_power",
+            "average_socket_power", "current_uclk", "average_uclk_frequency", "temperature_hotspot",
+            "temperature_mem", "gfx_activity", "average_gfx_activity", "throttle_status",
+            "indep_throttle_status"]
+    busy = sampler.summary(t0 + 0.2, t1 - 0.05, keys)
+    idle = sampler.summary(idle_t1 - 0.28, idle_t1, keys)
+    steps_per_unit = (case.seqlens.max() // S + 31) // 32
+    clk = None
+    for k in ("current_gfxclks_mean", "current_gfxclk", "average_gfxclk_frequency"):
+        if k in busy:
+            clk = busy[k]["median"]
+            break
+    return {
+        "clock_sample": kind, "workload": "v3_fp8_b64_l4096" if kind == "fp8" else HEADLINE,
+        "splits": S, "launches": n, "seconds": t1 - t0,
+        "kernel_us_median_of_batches": us,
+        "steps_per_unit": int(steps_per_unit),
+        "gfxclk_MHz_median": clk,
+        "cycles_per_step_at_that_clock": (us * 1e-6 * clk * 1e6 / steps_per_unit) if clk else None,
+        "busy": busy, "idle_before": idle,
+        "sampler_error": sampler.error,
+    }
+
+
 def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys).
@@ -378,6 +535,10 @@ def main():
     ap.add_argument("--crossover-T", default="1,8,32,64,96,128,160,192,256,384,512")
     ap.add_argument("--crossover-S", type=int, default=4096)
     ap.add_argument("--crossover-B", type=int, default=4)
+    ap.add_argument("--clock-sample", type=float, default=0.0,
+                    help="instead of the benchmark line: run the headline decode kernel back to back for this "
+                         "many seconds while sampling the gfx clock and power (one JSON line)")
+    ap.add_argument("--clock-kernel", choices=["bf16", "fp8"], default="bf16")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -398,6 +559,9 @@ def main():
         for row in crossover(Ts, args.crossover_S, args.crossover_B, max(3, min(args.steps, 20)),
                              max(1, min(args.warmup, 3)), dev):
             print(json.dumps(row), flush=True)
+        return
+    if args.clock_sample > 0:
+        print(json.dumps(clock_sample(args.clock_sample, args.clock_kernel, dev)), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
     case = synth.make_case(wl, poison=False)
@@ -604,9 +768,9 @@ def main():
         result["detail"].update(bench_fp8("v3_fp8_b64_l4096", 4, K, args.warmup, R, dev))
     if not args.no_cpu:
         try:
-            threads = min(16, len(os.sched_getaffinity(0)))
+            threads = len(os.sched_getaffinity(0))   # every host core this process may run on
         except AttributeError:
-            threads = min(16, os.cpu_count() or 1)
+            threads = os.cpu_count() or 1
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_pairs, threads,
                                               gpu_out=out.double().cpu().numpy())
     print(json.dumps(result), flush=True)

@@ -22,9 +22,9 @@
  *
  * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
  * written at their paged positions before the decode that reads them); for
- * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent;
- * for comparison, mla_decode_normal (the same function in the Normal,
- * per-head up-projected association order).
+ * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent.
+ * The same function in the Normal (per-head up-projected) association order,
+ * for comparison, is a separate library: mla_normal.h / libmla_normal.so.
  *
  * "M5.8" is the page "M5.8 - Multi-Head Latent Attention: Latent KV State,
  * Weight Absorption, and FlashMLA"; "mlxcel" is its "MLA absorbed decode" page.
@@ -38,7 +38,7 @@
  *    validate host-side scalars and pointers, enqueue their kernels on `stream`
  *    and return; they never synchronise, never allocate device memory and keep
  *    no state between calls -- except mla_validate_inputs (synchronous, for
- *    debugging) and mla_decode_normal (rocBLAS keeps a handle per device).
+ *    debugging).
  *    Calls on different streams that share no output or workspace buffer may
  *    run concurrently.
  *  - The return value is MLA_OK or a negative mla_status.  On a negative return
@@ -212,38 +212,6 @@ int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       const int32_t* topk_length, int B, int T, int H, int r, int d_R,
                       float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
                       float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
-                      float* lse, void* stream);
-
-/* Workspace of mla_decode_normal: the chunk's gathered latent and rope rows,
- * its up-projected keys and values ([B*chunk,H,128] bf16 each) and, with more
- * than one chunk (ceil(max_seqlen/chunk) > 1), the running state carried
- * between chunks.  B*chunk is at most 2^24. */
-int mla_normal_workspace_size(int B, int T, int H, int max_seqlen, int chunk, size_t* workspace_bytes);
-
-/* The Normal (non-absorbed) path on the GPU, for comparison with the absorbed
- * one: every cached latent is up-projected per head, k_nope = W_UK[h] c_j and
- * v_j = W_UV[h] c_j, and each head attends with the 192-wide key
- * [k_nope || k_pe] and the 128-wide value -- the same function as mla_absorb_q
- * + mla_decode_latent + mla_unabsorb_out, computed in the other association
- * order ("MLA in full detail", Steps 2-3 before the weights are folded; M5.8
- * 0x05 naive path).  The cache is processed `chunk` tokens per sequence at a
- * time (the chunked-KV form: rows gathered through the block table, two
- * rocBLAS GEMMs for the up-projection, an MFMA attention kernel that carries
- * the running max, sum and unnormalised output from chunk to chunk: the exact
- * log-sum-exp combination of M5.8 0x0C).
- *   q_nope [B,T,H,128], q_pe [B,T,H,64], w_uk, w_uv [H,128,512] bf16; cache,
- *   block_table, seqlens, max_seqlen, softmax_scale as for mla_decode_latent
- *   (causal over the T current rows).
- *   out [B,T,H,128] f32, lse [B,T,H] f32 (nullable).
- * rocBLAS keeps one handle per device (created on the first call, held until
- * the process ends, with rocBLAS's own workspace); this is the one entry point
- * that allocates.  Returns MLA_ERR_WORKSPACE when the workspace is missing or
- * smaller than mla_normal_workspace_size reports. */
-int mla_decode_normal(const uint16_t* q_nope, const uint16_t* q_pe, const uint16_t* w_uk,
-                      const uint16_t* w_uv, const uint16_t* kv_cache, int num_blocks, int page_size,
-                      const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens, int B,
-                      int T, int H, int d_nope, int d_R, int d_V, int r, int max_seqlen,
-                      float softmax_scale, int chunk, void* workspace, size_t workspace_bytes, float* out,
                       float* lse, void* stream);
 
 /* Merge of split partial states, per (b,t,h) over rows k in

@@ -15,8 +15,12 @@ Entry points (same names as the C ABI):
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
 * ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
 * ``mla_decode_sparse``  top-k latent attention over physical row ids (M5.8 0x0B)
-* ``mla_decode_normal``  the Normal path on the GPU (per-head K/V), for comparison
 * ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
+
+and, from the separate comparison library ``libmla_normal.so`` (``include/mla_normal.h``,
+which links rocBLAS and keeps its handle per device):
+
+* ``mla_decode_normal``  the Normal path on the GPU (per-head K/V), for comparison
 
 ``absorbed_decode`` chains the four calls for one decode step.
 """
@@ -29,12 +33,14 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla_latent.so")
+NORMAL_LIB_PATH = os.path.join(_HERE, "libmla_normal.so")
 
 MLA_BF16 = 0
 MLA_F32 = 1
 R_LATENT, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 
 _lib = None
+_normal_lib = None
 
 
 class MLAError(RuntimeError):
@@ -64,17 +70,31 @@ def load_library():
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
     L.mla_sparse_split_count.argtypes = [I, I, I, I, I, P]
-    L.mla_normal_workspace_size.argtypes = [I, I, I, I, I, P]
-    L.mla_decode_normal.argtypes = [P, P, P, P, P, I, I, P, I, P, I, I, I, I, I, I, I, I, F, I, P,
-                                     ctypes.c_size_t, P, P, P]
     L.mla_decode_sparse.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, F, I, P, I, P, P, P, I, P, P]
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
-                 "mla_decode_sparse", "mla_normal_workspace_size", "mla_decode_normal",
-                 "mla_validate_inputs", "mla_decode_latent_fp8"):
+                 "mla_decode_sparse", "mla_validate_inputs", "mla_decode_latent_fp8"):
         getattr(L, name).restype = I
     _lib = L
+    return L
+
+
+def load_normal_library():
+    """Load the in-tree Normal-path comparison library (rocBLAS GEMMs)."""
+    global _normal_lib
+    if _normal_lib is not None:
+        return _normal_lib
+    if not os.path.exists(NORMAL_LIB_PATH):
+        raise ImportError(f"{NORMAL_LIB_PATH} is not built; run mla_latent_kv_amd._build.build()")
+    L = ctypes.CDLL(NORMAL_LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.mla_normal_workspace_size.argtypes = [I, I, I, I, I, P]
+    L.mla_decode_normal.argtypes = [P, P, P, P, P, I, I, P, I, P, I, I, I, I, I, I, I, I, F, I, P,
+                                    ctypes.c_size_t, P, P, P]
+    L.mla_normal_workspace_size.restype = I
+    L.mla_decode_normal.restype = I
+    _normal_lib = L
     return L
 
 
@@ -175,6 +195,34 @@ class DecodeBuffers:
         self.split_indptr = torch.empty(B + 1, dtype=torch.int32, device=device)
 
 
+def _check_buffer(t, shape_ok, dtypes, device, what):
+    if t is None or not shape_ok(tuple(t.shape)) or t.dtype not in dtypes or t.device != device \
+            or not t.is_contiguous():
+        raise ValueError(what)
+
+
+def _check_decode_buffers(buf, B, T, H, max_seqlen, page_size, num_splits, device, what):
+    """A caller's DecodeBuffers must be large enough for THIS call: the kernels
+    write part_out / part_lse rows and split_indptr entries by the call's own
+    geometry (the C ABI sees no buffer sizes), so a buffer built for fewer
+    splits, sequences, tokens or heads would be written past its end."""
+    torch = _torch()
+    nbytes, rows = mla_decode_workspace_size(B, T, H, max_seqlen, page_size, num_splits)
+    rows = max(rows, 1)
+    _check_buffer(buf.part_out, lambda s: len(s) == 4 and s[0] >= rows and s[1:] == (T, H, R_LATENT),
+                  (torch.bfloat16, torch.float32), device,
+                  f"{what}: buffers.part_out must be [>= {rows}, {T}, {H}, {R_LATENT}] bf16/f32 on {device}")
+    _check_buffer(buf.part_lse, lambda s: len(s) == 3 and s[0] >= rows and s[1:] == (T, H),
+                  (torch.float32,), device, f"{what}: buffers.part_lse must be [>= {rows}, {T}, {H}] f32")
+    _check_buffer(buf.split_indptr, lambda s: len(s) == 1 and s[0] >= B + 1, (torch.int32,), device,
+                  f"{what}: buffers.split_indptr must hold >= {B + 1} int32")
+    if nbytes > 0:
+        _check_buffer(buf.workspace, lambda s: len(s) == 1 and s[0] >= nbytes, (torch.uint8,), device,
+                      f"{what}: buffers.workspace must hold >= {nbytes} bytes")
+        if buf.workspace_bytes < nbytes:
+            raise ValueError(f"{what}: buffers.workspace_bytes {buf.workspace_bytes} < {nbytes}")
+
+
 def mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
                       num_splits=1, out_dtype=None, buffers: Optional[DecodeBuffers] = None,
                       out_latent=None, lse=None, merge=True, stream=None):
@@ -226,8 +274,11 @@ def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softma
         out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
     if want_out and lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q_lat.device)
-    if num_splits != 1 and buffers is None:
-        buffers = DecodeBuffers(B, T, H, max_seqlen, page_size, num_splits, q_lat.device)
+    if num_splits != 1:
+        if buffers is None:
+            buffers = DecodeBuffers(B, T, H, max_seqlen, page_size, num_splits, q_lat.device)
+        else:
+            _check_decode_buffers(buffers, B, T, H, int(max_seqlen), page_size, int(num_splits), q_lat.device, what)
     ws = buffers.workspace if num_splits != 1 else None
     lib = load_library()
     st = (lib.mla_decode_latent_fp8 if fp8 else lib.mla_decode_latent)(
@@ -359,6 +410,18 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     if buffers is None:
         buffers = SparseBuffers(B, T, H, topk, num_splits, q_lat.device)
     S = buffers.num_splits
+    if S != mla_sparse_split_count(B, T, H, topk, num_splits):
+        raise ValueError(f"mla_decode_sparse: buffers hold {S} splits, the call asks for "
+                         f"{mla_sparse_split_count(B, T, H, topk, num_splits)}")
+    if S > 1:
+        rows = B * T * S
+        _check_buffer(buffers.part_out, lambda s: len(s) == 3 and s[0] >= rows and s[1:] == (H, R_LATENT),
+                      (torch.bfloat16, torch.float32), q_lat.device,
+                      f"mla_decode_sparse: buffers.part_out must be [>= {rows}, {H}, {R_LATENT}] bf16/f32")
+        _check_buffer(buffers.part_lse, lambda s: len(s) == 2 and s[0] >= rows and s[1] == H, (torch.float32,),
+                      q_lat.device, f"mla_decode_sparse: buffers.part_lse must be [>= {rows}, {H}] f32")
+        _check_buffer(buffers.split_indptr, lambda s: len(s) == 1 and s[0] >= B * T + 1, (torch.int32,),
+                      q_lat.device, f"mla_decode_sparse: buffers.split_indptr must hold >= {B * T + 1} int32")
     want_out = S == 1 or merge
     if want_out and out_latent is None:
         out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
@@ -378,7 +441,7 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
 
 def mla_normal_workspace_size(B, T, H, max_seqlen, chunk) -> int:
     nb = ctypes.c_size_t(0)
-    _check(load_library().mla_normal_workspace_size(B, T, H, max_seqlen, chunk, ctypes.byref(nb)),
+    _check(load_normal_library().mla_normal_workspace_size(B, T, H, max_seqlen, chunk, ctypes.byref(nb)),
            "mla_normal_workspace_size")
     return int(nb.value)
 
@@ -412,7 +475,7 @@ def mla_decode_normal(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, 
         out = torch.empty((B, T, H, dv), dtype=torch.float32, device=q_nope.device)
     if lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q_nope.device)
-    _check(load_library().mla_decode_normal(
+    _check(load_normal_library().mla_decode_normal(
         _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv), _ptr(kv_cache), num_blocks, page_size,
         _ptr(block_table), block_table.shape[1], _ptr(seqlens), B, T, H, dn, dr, dv, r, int(max_seqlen),
         float(softmax_scale), chunk, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
@@ -449,7 +512,7 @@ def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, ma
 
 
 __all__ = [
-    "MLA_BF16", "MLA_F32", "MLAError", "load_library", "status_string", "mla_status_string",
+    "MLA_BF16", "MLA_F32", "MLAError", "load_library", "load_normal_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
     "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
     "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",

@@ -1,4 +1,10 @@
-"""Builds libmla_latent.so (the HIP kernels + C ABI) in-tree with hipcc for gfx950."""
+"""Builds the shared libraries in-tree with hipcc for gfx950:
+
+* libmla_latent.so  -- the absorbed decode path (HIP kernels + C ABI of include/mla_latent.h);
+  depends on the HIP runtime only;
+* libmla_normal.so  -- the Normal-path comparison (include/mla_normal.h), whose
+  up-projection GEMMs are rocBLAS calls.
+"""
 from __future__ import annotations
 
 import os
@@ -10,9 +16,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_latent.so")
-SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip", "normal.hip"]
-# the Normal path's up-projection GEMMs are rocBLAS calls
-LINK_LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]
+NORMAL_LIB = os.path.join(HERE, "libmla_normal.so")
+# library -> (sources, extra link flags)
+LIBRARIES = {
+    LIB: (["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip"], []),
+    NORMAL_LIB: (["normal_api.cpp", "normal.hip"],
+                 ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]),
+}
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -34,14 +44,13 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source to an object (in parallel) and link the shared library."""
+    """Compile every source to an object (in parallel) and link the shared libraries."""
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     procs = []
-    objs = []
-    for src in SOURCES:
+    sources = sorted({src for srcs, _ in LIBRARIES.values() for src in srcs})
+    for src in sources:
         obj = os.path.join(BUILD, src + ".o")
-        objs.append(obj)
         cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"]
@@ -55,10 +64,11 @@ def build(verbose: bool = False) -> str:
             errors.append(f"{src}:\n{out.decode(errors='replace')}")
     if errors:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
-    tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *LINK_LIBS]
-    subprocess.check_call(link)
-    os.replace(tmp, LIB)
+    for lib, (srcs, flags) in LIBRARIES.items():
+        tmp = lib + ".tmp"
+        objs = [os.path.join(BUILD, src + ".o") for src in srcs]
+        subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *flags])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -34,6 +34,25 @@ def assert_close(got, ref, what=""):
     assert err <= t, f"{what}: max|err| {err} > tol {t}"
 
 
+# Absolute bound on lse.  A split's merge weight is exp(lse_k - M), so an lse
+# error d scales that weight by exp(d): |d| <= 1e-2 keeps every weight within
+# about 1% (the log-sum-exp merge contract of mlxcel "MLA absorbed decode",
+# Stage 2, and of M5.8 0x0C).  The output tolerance above, 1e-2 * max|lse| + 1e-3,
+# would allow 0.06-0.1 on lse values of 6-12 (ln of the context length).
+LSE_ABS_TOL = 1e-2
+
+
+def assert_lse_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(ref).all(), what
+    assert np.isfinite(got).all(), f"{what}: non-finite GPU lse"
+    err = float(np.max(np.abs(got - ref)))
+    log(f"  {what}: max|err| {err:.3e}  abs tol {LSE_ABS_TOL:.1e}  max|ref| {np.max(np.abs(ref)):.3e}")
+    assert err <= LSE_ABS_TOL, f"{what}: max|err| {err} > {LSE_ABS_TOL}"
+
+
 def bf16_tensor(bits, dev):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))

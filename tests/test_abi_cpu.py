@@ -1,6 +1,9 @@
-"""C-ABI checks that need no GPU: the library loads, exports every entry point
-include/mla_latent.h declares, and rejects bad host-side arguments before any
-launch (the pointers passed here are never dereferenced)."""
+"""C-ABI checks that need no GPU: the libraries load, export every entry point
+their headers declare (include/mla_latent.h -> libmla_latent.so,
+include/mla_normal.h -> libmla_normal.so), the decode library is free of
+rocBLAS and of mutable state, and every entry point rejects bad host-side
+arguments before any launch (the pointers passed here are never
+dereferenced)."""
 import ctypes
 import functools
 import os
@@ -12,29 +15,76 @@ import mla_latent_kv_amd as mk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mla_latent.h")
+NORMAL_HEADER = os.path.join(ROOT, "include", "mla_normal.h")
 
 OK, NULL, ALIGN, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4, -5
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(mk.LIB_PATH):
+    if not (os.path.exists(mk.LIB_PATH) and os.path.exists(mk.NORMAL_LIB_PATH)):
         from mla_latent_kv_amd import _build
         _build.build()
     return mk.load_library()
 
 
-def test_every_declared_symbol_is_exported(lib):
+@pytest.fixture(scope="module")
+def nlib(lib):
+    return mk.load_normal_library()
+
+
+def test_every_declared_symbol_is_exported(lib, nlib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_decode_latent", "mla_merge_splits", "mla_unabsorb_out"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
+    normal = set(declared_functions(NORMAL_HEADER)) - set(names)
+    assert normal == {"mla_decode_normal", "mla_normal_workspace_size"}
+    for n in normal:
+        assert hasattr(nlib, n), n
+        assert not hasattr(lib, n), f"{n} belongs to libmla_normal.so only"
+
+
+def _elf(cmd, path):
+    import shutil
+    import subprocess
+    if shutil.which(cmd[0]) is None:
+        pytest.skip(f"{cmd[0]} not available")
+    return subprocess.run([*cmd, path], check=True, capture_output=True, text=True).stdout
+
+
+def test_decode_library_links_no_rocblas(lib):
+    """libmla_latent.so depends on the HIP runtime only: no BLAS library (whose
+    handles and workspaces allocate) behind any of its entry points."""
+    needed = re.findall(r"NEEDED.*\[(.*)\]", _elf(["readelf", "-d"], mk.LIB_PATH))
+    assert needed and not [n for n in needed if "blas" in n.lower()], needed
+    assert any("rocblas" in n for n in re.findall(r"NEEDED.*\[(.*)\]", _elf(["readelf", "-d"], mk.NORMAL_LIB_PATH)))
+
+
+def test_decode_library_keeps_no_state(lib):
+    """No writable data of the library's own: the only writable symbols are the
+    toolchain's (ELF bookkeeping, the HIP fat-binary registration handles) and
+    the host-side handles of the kernels.  A rocBLAS handle table, a mutex or a
+    cached plan would show up here."""
+    syms = _elf(["nm", "-C", "--defined-only"], mk.LIB_PATH).splitlines()
+    own = []
+    for line in syms:
+        parts = line.split(maxsplit=2)
+        if len(parts) < 3 or parts[1] not in "BbDdSs":
+            continue
+        name = parts[2]
+        if name.startswith(("__", "_DYNAMIC", "_GLOBAL_OFFSET_TABLE_", "DW.ref.")):
+            continue
+        if re.fullmatch(r"mla::\w+_kernel(<.*>)?\(.*\)", name):   # kernel launch handles
+            continue
+        own.append(name)
+    assert not own, own
 
 
 def test_status_strings(lib):
@@ -141,6 +191,7 @@ def test_binding_names_match_abi():
     for n in ("mla_absorb_q", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
               "mla_unabsorb_out", "mla_append_cache",
               "mla_decode_sparse", "mla_sparse_split_count", "mla_decode_normal", "mla_normal_workspace_size",
+              "load_normal_library",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
         assert callable(getattr(mk, n))
 
@@ -220,7 +271,8 @@ def _normal(lib, **kw):
                                  a["out"], a["lse"], None)
 
 
-def test_normal_validation(lib):
+def test_normal_validation(nlib):
+    lib = nlib
     assert _normal(lib, dn=64) == UNSUP
     assert _normal(lib, r=256) == UNSUP
     assert _normal(lib, T=1025) == UNSUP
@@ -237,7 +289,8 @@ def test_normal_validation(lib):
     assert _normal(lib, B=0, qn=None, out=None, ws=None) == OK
 
 
-def test_normal_workspace_size(lib):
+def test_normal_workspace_size(nlib):
+    lib = nlib
     nb = ctypes.c_size_t(0)
     assert lib.mla_normal_workspace_size(4, 1, 128, 4096, 4096, ctypes.byref(nb)) == OK
     one = nb.value
@@ -310,3 +363,66 @@ def test_binding_rejects_host_tensors():
     bf = torch.bfloat16
     with pytest.raises(ValueError, match="device"):
         mk.mla_absorb_q(torch.zeros((1, 1, 1, 128), dtype=bf), torch.zeros((1, 128, 512), dtype=bf))
+
+
+def _decode_inputs(B=2, T=1, H=8, L=256, P=64):
+    import torch
+    bf = torch.bfloat16
+    nb = B * ((L + P - 1) // P)
+    return dict(q_lat=torch.zeros((B, T, H, 512), dtype=bf), q_pe=torch.zeros((B, T, H, 64), dtype=bf),
+                kv_cache=torch.zeros((nb, P, 576), dtype=bf),
+                block_table=torch.zeros((B, nb // B), dtype=torch.int32),
+                seqlens=torch.full((B,), L, dtype=torch.int32), max_seqlen=L)
+
+
+def _call_decode(inp, S, buffers):
+    return mk.mla_decode_latent(inp["q_lat"], inp["q_pe"], inp["kv_cache"], inp["block_table"], inp["seqlens"],
+                                inp["max_seqlen"], 0.07, num_splits=S, buffers=buffers, merge=False)
+
+
+@pytest.mark.parametrize("built_for", [dict(S=2), dict(B=1), dict(T=1, H=4), dict(part="shape")])
+def test_binding_rejects_decode_buffers_of_another_call(lib, built_for):
+    """A DecodeBuffers built for fewer splits, sequences or heads than the call
+    it is passed to would be written past its end by the kernels (the C ABI
+    sees no buffer sizes): the binding refuses it (CPU tensors: nothing is
+    launched either way)."""
+    import torch
+    inp = _decode_inputs(B=2, T=2, H=8)
+    B, T, H = 2, 2, 8
+    S = 4
+    kw = dict(B=B, T=T, H=H, S=S)
+    kw.update({k: v for k, v in built_for.items() if k != "part"})
+    buf = mk.DecodeBuffers(kw["B"], kw["T"], kw["H"], 256, 64, kw["S"], "cpu")
+    if built_for.get("part") == "shape":
+        buf.part_lse = torch.empty((buf.part_lse.shape[0], T, H + 1), dtype=torch.float32)
+    with pytest.raises(ValueError, match="buffers"):
+        _call_decode(inp, S, buf)
+
+
+def test_binding_accepts_matching_decode_buffers(lib):
+    """The same check passes buffers that fit (the call then stops at the
+    host-tensor check, before the C ABI)."""
+    inp = _decode_inputs(B=2, T=2, H=8)
+    for built_S in (4, 8):   # more splits than needed is also large enough
+        buf = mk.DecodeBuffers(2, 2, 8, 256, 64, built_S, "cpu")
+        with pytest.raises(ValueError, match="device"):
+            _call_decode(inp, 4, buf)
+
+
+def test_binding_rejects_sparse_buffers_of_another_call(lib):
+    import torch
+    bf = torch.bfloat16
+    B, T, H, topk = 2, 1, 8, 512
+    q = torch.zeros((B, T, H, 512), dtype=bf)
+    qp = torch.zeros((B, T, H, 64), dtype=bf)
+    kv = torch.zeros((16, 64, 576), dtype=bf)
+    idx = torch.zeros((B, T, topk), dtype=torch.int32)
+    with pytest.raises(ValueError, match="splits"):
+        mk.mla_decode_sparse(q, qp, kv, idx, None, 0.07, num_splits=4,
+                             buffers=mk.SparseBuffers(B, T, H, topk, 2, "cpu"))
+    small = mk.SparseBuffers(1, T, H, topk, 4, "cpu")      # built for one sequence
+    with pytest.raises(ValueError, match="buffers"):
+        mk.mla_decode_sparse(q, qp, kv, idx, None, 0.07, num_splits=4, buffers=small)
+    ok = mk.SparseBuffers(B, T, H, topk, 4, "cpu")
+    with pytest.raises(ValueError, match="device"):
+        mk.mla_decode_sparse(q, qp, kv, idx, None, 0.07, num_splits=4, buffers=ok)

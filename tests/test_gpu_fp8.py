@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import (SCALE, assert_close, bf16_tensor, bits_to_f64, log, sample_pairs, to_f64,
+from tests.gpu_util import (SCALE, assert_close, assert_lse_close, bf16_tensor, bits_to_f64, log, sample_pairs, to_f64,
                             upload)
 
 pytestmark = pytest.mark.gpu
@@ -72,7 +72,7 @@ def test_fp8_decode_unsplit(mk, name, out_f32):
     torch.cuda.synchronize()
     ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 @pytest.mark.parametrize("part", ["f32", "bf16"])
@@ -97,11 +97,11 @@ def test_fp8_split_partials_and_merge(mk, name, S, part):
     got_pl = buf.part_lse[:n].cpu().numpy().astype(np.float64)
     empty = np.isneginf(ref_pl)
     assert np.array_equal(np.isneginf(got_pl), empty), "empty partials must carry lse = -inf"
-    assert_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
+    assert_lse_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
     assert_close(to_f64(buf.part_out[:n]), ref_po, "partial out")
     ref_lat, ref_lse = oracle.latent_attention(bc, q64)
     assert_close(to_f64(lat), ref_lat, "merged latent")
-    assert_close(to_f64(lse), ref_lse, "merged lse")
+    assert_lse_close(to_f64(lse), ref_lse, "merged lse")
 
 
 def test_fp8_auto_split(mk):
@@ -114,7 +114,7 @@ def test_fp8_auto_split(mk):
     torch.cuda.synchronize()
     ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 def _single_rounding_agrees(f):
@@ -167,7 +167,7 @@ def test_fp8_end_to_end_vs_normal_path(mk):
     torch.cuda.synchronize()
     ref, ref_lse = oracle.normal_decode(bc)
     assert_close(to_f64(out), ref, "out")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 def test_fp8_full_headline_sampled(mk):
@@ -193,7 +193,7 @@ def test_fp8_full_headline_sampled(mk):
     got_lse = lse.cpu().numpy().astype(np.float64)
     for b, h in pairs:
         assert_close(got[b, :, h], ref_lat[b, :, h], f"latent b={b} h={h}")
-        assert_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
+        assert_lse_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
 
 
 def test_fp8_full_long_context_sampled(mk):
@@ -218,7 +218,7 @@ def test_fp8_full_long_context_sampled(mk):
     got_lse = lse.cpu().numpy().astype(np.float64)
     for b, h in pairs:
         assert_close(got[b, :, h], ref_lat[b, :, h], f"latent b={b} h={h}")
-        assert_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
+        assert_lse_close(got_lse[b, :, h], ref_lse[b, :, h], f"lse b={b} h={h}")
 
 
 @pytest.mark.parametrize("S", [1, 2, 0])
@@ -250,7 +250,7 @@ def test_fp8_score_growth_past_reference(mk, S, hot_token):
     hot = bits_to_f64(bc.kv_cache[blk, off, :512])
     assert float(np.max(np.abs(ref_lat[0, 0, 0] - hot))) < 1e-6 * float(np.max(np.abs(hot)))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 def test_fp8_auto_split_full_chip_runs_unsplit(mk):
@@ -269,7 +269,7 @@ def test_fp8_auto_split_full_chip_runs_unsplit(mk):
     assert bool((buf.part_lse == 123.0).all())
     ref_lat, ref_lse = oracle.latent_attention(bc, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 def test_fp8_page_placement_is_bitwise_invisible(mk):

@@ -1,15 +1,17 @@
 """GPU parity at the five workloads' full sizes, in the launch configuration the
-benchmark times (uniform 4-way split on the headline workload), checked on a
-seeded sample of (sequence, head) pairs that the CPU oracle computes one by one:
-the end-to-end chain against the Normal (decompressed) path, and the latent
-stage against the absorbed mirror on more pairs (its cost per pair is small).
-Unreadable cache rows are NaN-poisoned, so a stray read anywhere fails."""
+benchmark times (uniform 4-way split on the headline workload): the end-to-end
+chain against the Normal (decompressed) path on a seeded sample of (sequence,
+head) pairs that the CPU oracle computes one by one, and the latent stage
+(latent output and lse) against the fp64 absorbed mirror on EVERY (sequence,
+token, head) row (the mirror costs 2,176 FLOP per row and key, a few seconds
+per workload on the host cores).  Unreadable cache rows are NaN-poisoned, so a
+stray read anywhere fails."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import SCALE, assert_close, bits_to_f64, bf16_tensor, log, to_f64, upload, sample_pairs
+from tests.gpu_util import SCALE, assert_close, assert_lse_close, bits_to_f64, bf16_tensor, log, to_f64, upload, sample_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -45,22 +47,25 @@ def _run_chain(mk, case, d, S, part):
     return q_lat, out, lse
 
 
-def _check_pairs(got, ref, pairs, what):
+def _check_pairs(got, ref, pairs, what, check=assert_close):
     g = np.stack([got[b, :, h] for b, h in pairs])
     r = np.stack([ref[b, :, h] for b, h in pairs])
-    assert_close(g, r, what)
+    check(g, r, what)
 
 
-@pytest.mark.parametrize("name,S,part,n_normal,n_mirror", [
-    ("v2lite_tiny", 1, "-", 16, 16),
-    ("v3_b64_l4096", 4, "bf16", 10, 96),
-    ("v3_b64_l4096", 4, "f32", 4, 32),
-    ("v3_b64_l4096", 1, "-", 6, 32),
-    ("v3_ragged_b128", 0, "bf16", 6, 96),
-    ("v3_long_b4_l131072", 64, "f32", 3, 24),
-    ("v3_mtp_b32_t4_h32", 1, "-", 8, 64),
+@pytest.mark.parametrize("name,S,part,n_normal", [
+    ("v2lite_tiny", 1, "-", 16),
+    ("v3_b64_l4096", 4, "bf16", 10),
+    ("v3_b64_l4096", 4, "f32", 4),
+    ("v3_b64_l4096", 1, "-", 6),
+    ("v3_b64_l4096", 0, "bf16", 4),
+    ("v3_ragged_b128", 0, "bf16", 6),
+    ("v3_long_b4_l131072", 64, "f32", 3),
+    ("v3_long_b4_l131072", 64, "bf16", 2),
+    ("v3_mtp_b32_t4_h32", 1, "-", 8),
+    ("v3_mtp_b32_t4_h32", 0, "bf16", 4),
 ])
-def test_full_size(mk, name, S, part, n_normal, n_mirror):
+def test_full_size(mk, name, S, part, n_normal):
     log(f"[full] {name} num_splits={S} partials={part}: generating inputs")
     case = synth.make_case(W[name])
     d = upload(case)
@@ -74,7 +79,7 @@ def test_full_size(mk, name, S, part, n_normal, n_mirror):
     log(f"[full] {name}: Normal-path oracle on {len(pairs)} pairs")
     ref, ref_lse = oracle.normal_decode(case, pairs=pairs)
     _check_pairs(out_h, ref, pairs, "out (Normal path)")
-    _check_pairs(lse_h, ref_lse, pairs, "lse (Normal path)")
+    _check_pairs(lse_h, ref_lse, pairs, "lse (Normal path)", assert_lse_close)
 
     # latent stage on more pairs: seeded absorbed query given to both sides
     import torch
@@ -84,11 +89,10 @@ def test_full_size(mk, name, S, part, n_normal, n_mirror):
                                      num_splits=S, out_dtype=torch.float32,
                                      buffers=_buffers(mk, case, S, part))
     torch.cuda.synchronize()
-    mpairs = sample_pairs(case.B, case.H, n_mirror, seed=37)
-    log(f"[full] {name}: absorbed mirror on {len(mpairs)} pairs")
-    ref_lat, ref_lse2 = oracle.latent_attention(case, bits_to_f64(ql_bits), pairs=mpairs)
-    _check_pairs(to_f64(lat), ref_lat, mpairs, "latent (mirror)")
-    _check_pairs(to_f64(lse2), ref_lse2, mpairs, "lse (mirror)")
+    log(f"[full] {name}: absorbed mirror on all {case.B * case.T * case.H} rows")
+    ref_lat, ref_lse2 = oracle.latent_attention(case, bits_to_f64(ql_bits))
+    assert_close(to_f64(lat), ref_lat, "latent (mirror, every row)")
+    assert_lse_close(to_f64(lse2), ref_lse2, "lse (mirror, every row)")
 
 
 def test_headline_split_matches_unsplit_closely(mk):
@@ -104,4 +108,4 @@ def test_headline_split_matches_unsplit_closely(mk):
         res.append((to_f64(lat), to_f64(lse)))
     for k in (1, 2):
         assert_close(res[k][0], res[0][0], f"latent split variant {k}")
-        assert_close(res[k][1], res[0][1], f"lse split variant {k}")
+        assert_lse_close(res[k][1], res[0][1], f"lse split variant {k}")

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import (SCALE, assert_close, bf16_tensor, bits_to_f64, log, to_f64, upload)
+from tests.gpu_util import (SCALE, assert_close, assert_lse_close, bf16_tensor, bits_to_f64, log, to_f64, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +103,7 @@ def test_decode_unsplit(mk, name, out_f32):
     torch.cuda.synchronize()
     ref_lat, ref_lse = oracle.latent_attention(case, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 @pytest.mark.parametrize("latent_f32", [True, False])
@@ -140,7 +140,7 @@ def test_end_to_end_vs_normal_path(mk, name, S):
     torch.cuda.synchronize()
     ref, ref_lse = oracle.normal_decode(case)
     assert_close(to_f64(out), ref, "out")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 @pytest.mark.parametrize("part", ["f32", "bf16"])
@@ -169,11 +169,11 @@ def test_split_partials_and_merge(mk, name, S, part):
     got_pl = buf.part_lse[:n].cpu().numpy().astype(np.float64)
     empty = np.isneginf(ref_pl)
     assert np.array_equal(np.isneginf(got_pl), empty), "empty partials must carry lse = -inf"
-    assert_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
+    assert_lse_close(np.where(empty, 0, got_pl), np.where(empty, 0, ref_pl), "partial lse")
     assert_close(to_f64(buf.part_out[:n]), ref_po, "partial out")
     ref_lat, ref_lse = oracle.latent_attention(case, q64)
     assert_close(to_f64(lat), ref_lat, "merged latent")
-    assert_close(to_f64(lse), ref_lse, "merged lse")
+    assert_lse_close(to_f64(lse), ref_lse, "merged lse")
 
 
 def test_auto_split(mk):
@@ -188,7 +188,7 @@ def test_auto_split(mk):
     torch.cuda.synchronize()
     ref_lat, ref_lse = oracle.latent_attention(case, bits_to_f64(ql_bits))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 @pytest.mark.parametrize("part", ["f32", "bf16"])
@@ -215,7 +215,38 @@ def test_merge_of_oracle_partials(mk, part):
                                    torch.from_numpy(plan[0]).to(dev), case.B,
                                    out_dtype=torch.float32)
     assert_close(to_f64(out), ref, "merged")
-    assert_close(to_f64(lse), ref_lse, "merged lse")
+    assert_lse_close(to_f64(lse), ref_lse, "merged lse")
+
+
+def test_merge_of_log2_lse_fails_parity(mk):
+    """Negative control on the GPU (mlxcel "MLA absorbed decode", Stage 2: an
+    lse in log2 units merges into a plausible but wrong average).  The merge
+    kernel is given the oracle's partials with their lse converted to log2
+    units: its output must FAIL the product tolerance against the exact merge,
+    while the same call with natural-log lse passes it.  Partials are drawn so
+    that the splits' lse values differ by several units, where the wrong base
+    changes the weights by far more than the tolerance."""
+    import torch
+    log("[merge] negative control: log2-unit lse")
+    case = _case("mtp_t4_h32")
+    q64 = bits_to_f64(_stage_q_lat(case, 7310)) * 3.0   # sharper scores: lse spread across splits
+    plan = oracle.split_plan(case.seqlens, 4, case.page_size)
+    po, pl = oracle.latent_attention(case, q64, plan=plan)
+    dev = "cuda:0"
+    po32 = po.astype(np.float32)
+    ref, _ = oracle.merge(po32.astype(np.float64), pl.astype(np.float32).astype(np.float64), plan[0])
+    t_po = torch.from_numpy(po32).to(dev)
+    ind = torch.from_numpy(plan[0]).to(dev)
+    good, _ = mk.mla_merge_splits(t_po, torch.from_numpy(pl.astype(np.float32)).to(dev), ind, case.B,
+                                  out_dtype=torch.float32)
+    assert_close(to_f64(good), ref, "merged (natural-log lse)")
+    pl2 = np.where(np.isfinite(pl), pl / np.log(2.0), pl).astype(np.float32)
+    bad, _ = mk.mla_merge_splits(t_po, torch.from_numpy(pl2).to(dev), ind, case.B, out_dtype=torch.float32)
+    err = float(np.max(np.abs(to_f64(bad) - ref)))
+    t = 1e-2 * float(np.max(np.abs(ref))) + 1e-3
+    log(f"  log2-unit lse: max|err| {err:.3e} against tol {t:.3e} (must exceed it)")
+    assert np.isfinite(to_f64(bad)).all()
+    assert err > t, "a merge fed log2-unit lse passed parity: the control does not discriminate"
 
 
 def _hot_key_case(name, seed, hot_token, gain=16):
@@ -252,7 +283,7 @@ def test_score_growth_past_reference(mk, S, hot_token):
                                     hot_token % case.page_size, :512])
     assert float(np.max(np.abs(ref_lat[0, 0, 0] - hot))) < 1e-9 * float(np.max(np.abs(hot)))
     assert_close(to_f64(lat), ref_lat, "latent")
-    assert_close(to_f64(lse), ref_lse, "lse")
+    assert_lse_close(to_f64(lse), ref_lse, "lse")
 
 
 def test_page_placement_is_bitwise_invisible(mk):

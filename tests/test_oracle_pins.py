@@ -44,55 +44,57 @@ def rel(a, b):
 
 
 # --------------------------------------------------------------------------
-# 1. the page's own parity script
+# 1. the associativity identity the absorbed form rests on
 
-def test_page_numpy_script_shapes_and_identity():
-    """"MLA in full detail", numpy parity script: queries 3, context 5, rank 4,
-    key_dim 2, value_dim 3, rope_dim 2, seed 42.  The script states its identity
-    with row vectors (k = c @ uk); the oracle stores W_UK[h] = uk^T
-    (column convention of M5.8 0x04).  Each query sees all 5 keys, which the
-    oracle expresses as 3 sequences of length 5 with T = 1."""
-    rng = np.random.default_rng(42)
-    queries, context, rank, key_dim, value_dim, rope_dim = 3, 5, 4, 2, 3, 2
-    c = rng.normal(size=(context, rank))
-    q = rng.normal(size=(queries, key_dim))
-    q_rope = rng.normal(size=(queries, rope_dim))
-    k_rope = rng.normal(size=(context, rope_dim))
-    uk = rng.normal(size=(rank, key_dim))
-    uv = rng.normal(size=(rank, value_dim))
-    bf = lambda x: synth.f32_to_bf16_bits(x.astype(np.float32))
-    f = lambda bits: oracle.bf16_to_f64(bits)
-    c_b, q_b, qr_b, kr_b, uk_b, uv_b = map(bf, (c, q, q_rope, k_rope, uk, uv))
-    # the script's formulas on the same (bf16-representable) values
-    C, Q, QR, KR, UK, UV = map(f, (c_b, q_b, qr_b, kr_b, uk_b, uv_b))
-    scale = (key_dim + rope_dim) ** -0.5
-    expanded_scores = (Q @ (C @ UK).T + QR @ KR.T) * scale
-    absorbed_scores = ((Q @ UK.T) @ C.T + QR @ KR.T) * scale
-    np.testing.assert_allclose(absorbed_scores, expanded_scores, atol=1e-12)
-    e = np.exp(expanded_scores - expanded_scores.max(-1, keepdims=True))
-    a = e / e.sum(-1, keepdims=True)
-    script_out = a @ (C @ UV)
-    np.testing.assert_allclose(script_out, (a @ C) @ UV, atol=1e-12)
-    script_lse = np.log(np.exp(expanded_scores).sum(-1))
+def test_absorbed_equals_expanded_attention_on_a_tiny_head():
+    """"MLA in full detail" (the absorbed form and its numpy parity check)
+    states that folding the key up-projection into the query leaves every
+    score unchanged and folding the value up-projection behind the softmax
+    leaves the output unchanged.  Checked with this project's own draws: four
+    query tokens against seven cached rows of latent rank 6 (key part 3,
+    value 5, rope 2).  A direct matrix evaluation of the expanded attention
+    (explicit per-key K = [W_UK c || k_pe] and V = W_UV c), the oracle's
+    Normal path and its absorbed mirror agree to 1e-12."""
+    rng = np.random.default_rng(2024)
+    n_q, n_k, rank, d_key, d_val, d_rope = 4, 7, 6, 3, 5, 2
 
-    # same numbers through the oracle
+    def draw(*shape):
+        return synth.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+    lat_b, qn_b, qp_b, kp_b = draw(n_k, rank), draw(n_q, d_key), draw(n_q, d_rope), draw(n_k, d_rope)
+    wk_b, wv_b = draw(d_key, rank), draw(d_val, rank)          # W_UK[h], W_UV[h] of the one head
+    lat, qn, qp, kp, wk, wv = (oracle.bf16_to_f64(x) for x in (lat_b, qn_b, qp_b, kp_b, wk_b, wv_b))
+
+    keys = np.concatenate([lat @ wk.T, kp], axis=1)           # [n_k, d_key + d_rope]
+    vals = lat @ wv.T                                          # [n_k, d_val]
+    qry = np.concatenate([qn, qp], axis=1)
+    scores = qry @ keys.T / np.sqrt(d_key + d_rope)
+    wts = np.exp(scores - scores.max(1, keepdims=True))
+    wts /= wts.sum(1, keepdims=True)
+    ref_out = wts @ vals
+    ref_lse = scores.max(1) + np.log(np.exp(scores - scores.max(1, keepdims=True)).sum(1))
+    # the identity itself, both sides
+    np.testing.assert_allclose((qn @ wk) @ lat.T, qn @ keys[:, :d_key].T, atol=1e-12)
+    np.testing.assert_allclose((wts @ lat) @ wv.T, ref_out, atol=1e-12)
+
+    # the same numbers through the oracle: every query token its own sequence
+    # (T = 1) of length n_k, one page of 8 rows
     from types import SimpleNamespace
-    row = np.concatenate([c_b, kr_b], axis=1)           # [5, rank + rope]
+    rows = np.concatenate([lat_b, kp_b], axis=1)
     case = SimpleNamespace(
-        B=queries, T=1, H=1, page_size=8, num_blocks=1, max_blocks=1,
-        q_nope=q_b.reshape(queries, 1, 1, key_dim), q_pe=qr_b.reshape(queries, 1, 1, rope_dim),
-        w_uk=np.ascontiguousarray(uk_b.T).reshape(1, key_dim, rank),
-        w_uv=np.ascontiguousarray(uv_b.T).reshape(1, value_dim, rank),
-        kv_cache=np.concatenate([row, np.zeros((3, rank + rope_dim), np.uint16)]).reshape(1, 8, -1),
-        block_table=np.zeros((queries, 1), np.int32), seqlens=np.full(queries, context, np.int32))
+        B=n_q, T=1, H=1, page_size=8, num_blocks=1, max_blocks=1,
+        q_nope=qn_b.reshape(n_q, 1, 1, d_key), q_pe=qp_b.reshape(n_q, 1, 1, d_rope),
+        w_uk=wk_b.reshape(1, d_key, rank), w_uv=wv_b.reshape(1, d_val, rank),
+        kv_cache=np.concatenate([rows, np.zeros((8 - n_k, rank + d_rope), np.uint16)]).reshape(1, 8, -1),
+        block_table=np.zeros((n_q, 1), np.int32), seqlens=np.full(n_q, n_k, np.int32))
     out, lse = oracle.normal_decode(case)
-    np.testing.assert_allclose(out[:, 0, 0, :], script_out, rtol=0, atol=1e-12)
-    np.testing.assert_allclose(lse[:, 0, 0], script_lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out[:, 0, 0, :], ref_out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, 0, 0], ref_lse, rtol=0, atol=1e-12)
     ql = oracle.absorb(case.q_nope, case.w_uk)
-    lat, lse2 = oracle.latent_attention(case, ql)
-    np.testing.assert_allclose(lat[:, 0, 0, :], a @ C, atol=1e-12)
-    out2 = oracle.unabsorb(lat, case.w_uv)
-    np.testing.assert_allclose(out2[:, 0, 0, :], script_out, atol=1e-12)
+    np.testing.assert_allclose(ql[:, 0, 0, :], qn @ wk, atol=1e-12)
+    lat_out, lse2 = oracle.latent_attention(case, ql)
+    np.testing.assert_allclose(lat_out[:, 0, 0, :], wts @ lat, atol=1e-12)
+    np.testing.assert_allclose(oracle.unabsorb(lat_out, case.w_uv)[:, 0, 0, :], ref_out, atol=1e-12)
     np.testing.assert_allclose(lse2, lse, atol=1e-12)
 
 
