@@ -448,6 +448,71 @@ def clock_sample(seconds, kind, dev):
     }
 
 
+def power_roof(seconds, dev):
+    """Practical roofs under the power limit (context for the roofline line):
+    the probe kernel of libmla_probe.so run back to back for `seconds` per
+    mode -- MFMAs only, HBM stream only, both at the decode's FLOP/byte
+    (one 1 KB load per 7 MFMAs of 32x32x16: 224 FLOP/B against the headline's
+    228), and
+    the same with one LDS operand read per MFMA -- each with the gfx clock and
+    socket power it ran at."""
+    import ctypes
+    import numpy as np
+    import torch
+    from mla_latent_kv_amd import _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.mla_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    grid, slice_ = 256, 4 << 20
+    src = torch.ones(grid * slice_, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = []
+    for name, mode, ratio, iters in (("mfma_only", 0, 7, 16000), ("hbm_stream_only", 1, 7, 6000),
+                                     ("mfma_and_stream_224_flop_per_byte", 2, 7, 10000),
+                                     ("mfma_stream_and_lds_reads_224_flop_per_byte", 3, 7, 10000)):
+        def launch():
+            st = lib.mla_probe_launch(ctypes.c_void_p(src.data_ptr()), slice_, grid, iters, mode, ratio,
+                                      ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"probe launch failed: hipError {st}")
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        sampler = MetricsSampler().start()
+        time.sleep(0.2)
+        evs = []
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(8):
+                launch()
+            e1.record(stream)
+            evs.append((e0, e1))
+            if len(evs) > 2:
+                evs[-3][1].synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sampler.stop()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs[1:]])) / 8
+        waves = grid * 4
+        flops = waves * 4 * iters * 32768 if mode != 1 else 0
+        loads = iters if mode == 1 else (4 * iters) // ratio if mode >= 2 else 0
+        nbytes = waves * loads * 1024
+        summ = sampler.summary(t0 + 0.3, t1 - 0.05, ["current_gfxclks_mean", "current_socket_power"])
+        clk = summ.get("current_gfxclks_mean", {}).get("median")
+        out.append({"probe": name, "launch_ms": ms, "TFLOPs": flops / (ms * 1e-3) / 1e12,
+                    "GBps": nbytes / (ms * 1e-3) / 1e9, "gfxclk_MHz": clk,
+                    "socket_power_W": summ.get("current_socket_power", {}).get("median"),
+                    "mfma_duty_at_that_clock": (flops / (ms * 1e-3)) / (256 * 4096 * clk * 1e6) if clk and flops
+                    else None,
+                    "sampler_error": sampler.error})
+    del src
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys).
@@ -508,6 +573,134 @@ def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     }
 
 
+def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
+    """Time one workload's step (absorb -> decode -> merge -> un-absorb) on the
+    GPU: R replicas of the cache and weights rotate from step to step; K eager
+    steps with HIP events around the decode launch on its stream give the
+    decode kernel's own duration (with automatic splits it includes the
+    one-workgroup plan kernel); K replays of the step captured as a HIP graph
+    (one per replica) give the chain's time per step."""
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    case = synth.make_case(wl, poison=False)
+    B, T, H = case.B, case.T, case.H
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv0 = bf16(case.kv_cache)
+    kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
+    wuk0, wuv0 = bf16(case.w_uk), bf16(case.w_uv)
+    wuk = [wuk0] + [wuk0.clone() for _ in range(R - 1)]
+    wuv = [wuv0] + [wuv0.clone() for _ in range(R - 1)]
+    q_nope, q_pe = bf16(case.q_nope), bf16(case.q_pe)
+    block_table = torch.from_numpy(case.block_table).to(dev)
+    seqlens = torch.from_numpy(case.seqlens).to(dev)
+    max_seqlen = case.max_seqlen
+    scale = mk.softmax_scale()
+    part_dtype = torch.bfloat16 if partials == "bf16" else torch.float32
+    buf = mk.DecodeBuffers(B, T, H, max_seqlen, case.page_size, S, dev, part_dtype=part_dtype) \
+        if S != 1 else None
+    q_lat = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
+    latent = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(r, ev=None):
+        mk.mla_absorb_q(q_nope, wuk[r], q_lat=q_lat)
+        if ev is not None:
+            ev[0].record(stream)
+        if S == 1:
+            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
+                                 num_splits=1, out_latent=latent, lse=lse)
+        else:
+            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
+                                 num_splits=S, buffers=buf, merge=False)
+        if ev is not None:
+            ev[1].record(stream)
+        if S != 1:
+            mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, B, out_latent=latent,
+                                lse=lse)
+        mk.mla_unabsorb_out(latent, wuv[r], out=out)
+
+    for i in range(W):
+        step(i % R)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    res = {"case": case, "kv": kv, "block_table": block_table, "seqlens": seqlens, "out": out,
+           "dec_ms": [a.elapsed_time(b) for a, b in evs], "eager_ms_per_step": (t1 - t0) * 1e3 / K,
+           "warm_ms": None}
+    if warm:
+        # the same with one cache replica (no rotation: the 256 MB last-level cache
+        # may serve part of a step's reads from the previous step) -- context only
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            step(0, wev[i])
+        torch.cuda.synchronize()
+        res["warm_ms"] = float(np.median([a.elapsed_time(b) for a, b in wev]))
+    res["ms_per_step"] = res["eager_ms_per_step"]
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(R):
+                step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        for i in range(W):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        res["ms_per_step"] = (t1 - t0) * 1e3 / K
+        res["graphs"] = graphs
+    return res
+
+
+def workload_line(wl, S, partials, K, W, R, dev):
+    """Timed figures of one workload (the other configurations beside the
+    headline): decode kernel time and its algorithmic rates, chain time and
+    query tokens per second."""
+    import numpy as np
+    import torch
+    tw = time_workload(wl, S, partials, K, W, R, dev, graph=True)
+    case = tw["case"]
+    dec_ms = float(np.mean(tw["dec_ms"]))
+    nbytes, flops = decode_algorithmic(case)
+    rec = {
+        "B": case.B, "T": case.T, "H": case.H, "L": wl.L, "context_tokens": int(np.sum(case.seqlens)),
+        "page_size": case.page_size, "num_splits": S, "partials": partials, "cache_replicas": R, "steps": K,
+        "decode_us": dec_ms * 1e3, "decode_us_median": float(np.median(tw["dec_ms"])) * 1e3,
+        "decode_alg_bytes": nbytes, "decode_alg_flops": flops,
+        "decode_GBps": nbytes / (dec_ms * 1e-3) / 1e9,
+        "decode_hbm_frac": nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "decode_tflops": flops / (dec_ms * 1e-3) / 1e12,
+        "decode_mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "chain_us_per_step": tw["ms_per_step"] * 1e3,
+        "tokens_per_s": case.B * case.T / (tw["ms_per_step"] * 1e-3),
+        "chain_TBps": chain_algorithmic(case, nbytes) / (tw["ms_per_step"] * 1e-3) / 1e12,
+    }
+    del tw
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,6 +732,14 @@ def main():
                     help="instead of the benchmark line: run the headline decode kernel back to back for this "
                          "many seconds while sampling the gfx clock and power (one JSON line)")
     ap.add_argument("--clock-kernel", choices=["bf16", "fp8"], default="bf16")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the driver-timed lines of the other configurations (detail.workloads)")
+    ap.add_argument("--roof-seconds", type=float, default=1.0,
+                    help="seconds per practical-roof probe and half the seconds of the decode clock sample "
+                         "reported under detail (0 skips them)")
+    ap.add_argument("--power-roof", type=float, default=0.0,
+                    help="instead of the benchmark line: run the practical-roof probes for this many seconds each "
+                         "(one JSON line per probe)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -560,105 +761,26 @@ def main():
                              max(1, min(args.warmup, 3)), dev):
             print(json.dumps(row), flush=True)
         return
+    if args.power_roof > 0:
+        for row in power_roof(args.power_roof, dev):
+            print(json.dumps(row), flush=True)
+        return
     if args.clock_sample > 0:
         print(json.dumps(clock_sample(args.clock_sample, args.clock_kernel, dev)), flush=True)
         return
     wl = synth.WORKLOADS[args.workload]
-    case = synth.make_case(wl, poison=False)
-    B, T, H = case.B, case.T, case.H
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    R = max(1, args.replicas)
-    kv0 = bf16(case.kv_cache)
-    kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
-    wuk0, wuv0 = bf16(case.w_uk), bf16(case.w_uv)
-    wuk = [wuk0] + [wuk0.clone() for _ in range(R - 1)]
-    wuv = [wuv0] + [wuv0.clone() for _ in range(R - 1)]
-    q_nope, q_pe = bf16(case.q_nope), bf16(case.q_pe)
-    block_table = torch.from_numpy(case.block_table).to(dev)
-    seqlens = torch.from_numpy(case.seqlens).to(dev)
-    max_seqlen = case.max_seqlen
-    scale = mk.softmax_scale()
-
-    S = args.splits
-    part_dtype = torch.bfloat16 if args.partials == "bf16" else torch.float32
-    buf = mk.DecodeBuffers(B, T, H, max_seqlen, case.page_size, S, dev, part_dtype=part_dtype) \
-        if S != 1 else None
-    q_lat = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
-    latent = torch.empty((B, T, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(r, ev=None):
-        mk.mla_absorb_q(q_nope, wuk[r], q_lat=q_lat)
-        if ev is not None:
-            ev[0].record(stream)
-        if S == 1:
-            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
-                                 num_splits=1, out_latent=latent, lse=lse)
-        else:
-            mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
-                                 num_splits=S, buffers=buf, merge=False)
-        if ev is not None:
-            ev[1].record(stream)
-        if S != 1:
-            mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, B, out_latent=latent,
-                                lse=lse)
-        mk.mla_unabsorb_out(latent, wuv[r], out=out)
-
-    for i in range(args.warmup):
-        step(i % R)
-    torch.cuda.synchronize()
-
     K = args.steps
-    # decode-kernel time: HIP events around the decode launch of eager steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i % R, evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eager_ms_per_step = (t1 - t0) * 1e3 / K
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    R = max(1, args.replicas)
+    S = args.splits
+    tw = time_workload(wl, S, args.partials, K, args.warmup, R, dev, graph=not args.no_graph, warm=True)
+    case, kv, block_table, seqlens, out = tw["case"], tw["kv"], tw["block_table"], tw["seqlens"], tw["out"]
+    B, T, H = case.B, case.T, case.H
+    stream = torch.cuda.current_stream()
+    dec_ms = tw["dec_ms"]
     dec_ms_avg = float(np.mean(dec_ms))
-
-    # the same with one cache replica (no rotation: the 256 MB last-level cache
-    # may serve part of a step's reads from the previous step) -- context only
-    warm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    for i in range(K):
-        step(0, warm[i])
-    torch.cuda.synchronize()
-    warm_ms = float(np.median([a.elapsed_time(b) for a, b in warm]))
-
-    # whole chain: one captured HIP graph per cache replica (the four launches of
-    # a step as graph nodes), replayed back to back
-    ms_per_step = eager_ms_per_step
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for r in range(R):
-                step(r)
-        torch.cuda.current_stream().wait_stream(side)
-        graphs = []
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(r)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / K
+    eager_ms_per_step = tw["eager_ms_per_step"]
+    warm_ms = tw["warm_ms"]
+    ms_per_step = tw["ms_per_step"]
 
     # cache append of the step's new rows (written at position L - T + t of each
     # sequence; the timed cache's own rows there are overwritten, which changes
@@ -762,6 +884,22 @@ def main():
             "append_GBps": app_bytes / (app_ms * 1e-3) / 1e9,
         },
     }
+    if not args.no_workloads:
+        # every other configuration, timed (fewer steps each), plus the
+        # headline with fp32 partials (the partial dtype the scope table names)
+        Kw, Ww = min(K, 30), min(args.warmup, 5)
+        others = [("v2lite_tiny", "v2lite_tiny", 1, "bf16", 3),
+                  ("v3_b64_l4096_f32_partials", HEADLINE, 4, "f32", 3),
+                  ("v3_ragged_b128", "v3_ragged_b128", 0, "bf16", 2),
+                  ("v3_long_b4_l131072", "v3_long_b4_l131072", 64, "bf16", 2),
+                  ("v3_mtp_b32_t4_h32", "v3_mtp_b32_t4_h32", 0, "bf16", 3)]
+        lines = {}
+        for key, name, S_w, part, R_w in others:
+            lines[key] = workload_line(synth.WORKLOADS[name], S_w, part, Kw, Ww, R_w, dev)
+        result["detail"]["workloads"] = lines
+    if args.roof_seconds > 0:
+        result["detail"]["decode_clock_sample"] = clock_sample(args.roof_seconds * 2, "bf16", dev)
+        result["detail"]["power_roof"] = power_roof(args.roof_seconds, dev)
     if not args.no_sparse:
         result["detail"].update(bench_sparse("v3_sparse_b64_topk2048", K, args.warmup, R, dev))
     if not args.no_fp8:

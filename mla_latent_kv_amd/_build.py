@@ -3,7 +3,9 @@
 * libmla_latent.so  -- the absorbed decode path (HIP kernels + C ABI of include/mla_latent.h);
   depends on the HIP runtime only;
 * libmla_normal.so  -- the Normal-path comparison (include/mla_normal.h), whose
-  up-projection GEMMs are rocBLAS calls.
+  up-projection GEMMs are rocBLAS calls;
+* libmla_probe.so   -- the benchmark's practical-roof probe (csrc/roof_probe.hip),
+  not part of the decode path.
 """
 from __future__ import annotations
 
@@ -17,11 +19,13 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_latent.so")
 NORMAL_LIB = os.path.join(HERE, "libmla_normal.so")
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 # library -> (sources, extra link flags)
 LIBRARIES = {
     LIB: (["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip"], []),
     NORMAL_LIB: (["normal_api.cpp", "normal.hip"],
                  ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]),
+    PROBE_LIB: (["roof_probe.hip"], []),
 }
 ARCH = "gfx950"
 

@@ -1,0 +1,126 @@
+// Practical roofs of the part under its power limit, for the benchmark's
+// context lines (not part of the decode path; built into libmla_probe.so).
+//
+// One workgroup of four waves per CU (160 KB of LDS each, as the decode
+// kernel).  Each wave runs `iters` groups of four independent bf16 MFMAs
+// 32x32x16 and, depending on the mode:
+//   mode 0  the MFMAs only;
+//   mode 1  1 KB direct-to-LDS loads from HBM only (`iters` of them);
+//   mode 2  the MFMAs plus one 1 KB load after every `ratio` MFMAs
+//           (floor(4 iters / ratio) loads: 32768 * ratio / 1024 FLOP per byte);
+//   mode 3  as mode 2, plus one 16-byte-per-lane LDS read (1 KB per wave)
+//           feeding each MFMA's B operand, read one group ahead (about the
+//           decode kernel's LDS operand traffic per MFMA).
+// Workgroup g streams its own slice [g * slice, (g + 1) * slice) of `src`
+// (at most 24 loads in flight per wave).  The work per launch is known
+// exactly, so rate = work / duration; a long run of launches, sampled for
+// clock and power, gives the MFMA rate and the HBM rate the part sustains at
+// its power limit for a given FLOP/byte mix.
+//
+// extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters,
+//                                 int mode, int ratio, float* sink, void* stream)
+//   src: device buffer of at least grid * slice bytes, slice a multiple of 4 KB
+//   and at least 4 KB; iters even; ratio 1..64; sink: 256 floats (never
+//   written for these inputs; keeps the results live).  Returns a hipError_t.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds_addr)
+               : "memory");
+}
+
+constexpr int kLds = 160 * 1024;
+
+__global__ __launch_bounds__(256, 1) void roof_kernel(const uint8_t* src, size_t slice, int iters, int mode,
+                                                      int ratio, float* sink) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  const uint32_t win = lds_base + (uint32_t)(w * 32768);   // this wave's 32 KB of the first 128 KB
+  f32x16 a0 = {}, a1 = {}, a2 = {}, a3 = {};
+  bf16x8 x, y;
+  for (int e = 0; e < 8; ++e) {
+    x[e] = (__bf16)(0.001f * (l + e));
+    y[e] = (__bf16)(0.002f * (l - e));
+  }
+  const uint8_t* base = src + (size_t)blockIdx.x * slice;
+  const uint32_t nblk = (uint32_t)(slice / 1024);   // >= 4
+  uint32_t blk = (uint32_t)w;
+  uint32_t slot = 0;
+  auto load = [&]() {
+    dma16s(blk * 1024u + 16u * (uint32_t)l, base, __builtin_amdgcn_readfirstlane(win + slot * 1024u));
+    slot = (slot + 1) & 31u;
+    blk += 4;
+    if (blk >= nblk) blk = (uint32_t)w;
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  };
+  int credit = 0;
+  auto loads_due = [&]() {
+    credit += 4;
+    while (credit >= ratio) {
+      credit -= ratio;
+      load();
+    }
+  };
+  auto group = [&](const bf16x8& b0, const bf16x8& b1, const bf16x8& b2, const bf16x8& b3) {
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b0, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b1, a1, 0, 0, 0);
+    a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b2, a2, 0, 0, 0);
+    a3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b3, a3, 0, 0, 0);
+  };
+  auto rd16 = [&](uint32_t off) {
+    return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(win + (off & 32767u) + 16u * (uint32_t)l);
+  };
+  if (mode == 0) {
+    for (int i = 0; i < iters; ++i) group(y, y, y, y);
+  } else if (mode == 1) {
+    for (int i = 0; i < iters; ++i) load();
+  } else if (mode == 2) {
+    for (int i = 0; i < iters; ++i) {
+      group(y, y, y, y);
+      loads_due();
+    }
+  } else {
+    // two groups per iteration: group A uses ya (while yb is read), group B yb
+    uint32_t off = 0;
+    bf16x8 ya0 = rd16(off), ya1 = rd16(off + 1024), ya2 = rd16(off + 2048), ya3 = rd16(off + 3072);
+    off += 4096;
+    for (int i = 0; i < iters; i += 2) {
+      const bf16x8 yb0 = rd16(off), yb1 = rd16(off + 1024), yb2 = rd16(off + 2048), yb3 = rd16(off + 3072);
+      group(ya0, ya1, ya2, ya3);
+      loads_due();
+      ya0 = rd16(off + 4096);
+      ya1 = rd16(off + 5120);
+      ya2 = rd16(off + 6144);
+      ya3 = rd16(off + 7168);
+      group(yb0, yb1, yb2, yb3);
+      loads_due();
+      off += 8192;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float s = 0.f;
+  for (int e = 0; e < 16; ++e) s += a0[e] + a1[e] + a2[e] + a3[e];
+  if (s == 1.2345e30f) sink[threadIdx.x] = s;   // never true for these inputs: keeps the MFMAs live
+}
+
+}  // namespace
+
+extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters, int mode, int ratio,
+                                float* sink, void* stream) {
+  if (!src || !sink || grid < 1 || iters < 2 || iters % 2 || mode < 0 || mode > 3 || ratio < 1 || ratio > 64 ||
+      slice < 4096 || slice % 4096)
+    return (int)hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute((const void*)roof_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(roof_kernel, dim3(grid), dim3(256), kLds, (hipStream_t)stream, (const uint8_t*)src, slice,
+                     iters, mode, ratio, sink);
+  return (int)hipGetLastError();
+}
