@@ -38,7 +38,8 @@
  *    validate host-side scalars and pointers, enqueue their kernels on `stream`
  *    and return; they never synchronise, never allocate device memory and keep
  *    no state between calls -- except mla_validate_inputs (synchronous, for
- *    debugging).
+ *    debugging) and mla_decode_latent_noalloc (a device array of its own per
+ *    GPU, whose address it keeps per device).
  *    Calls on different streams that share no output or workspace buffer may
  *    run concurrently.
  *  - The return value is MLA_OK or a negative mla_status.  On a negative return
@@ -183,6 +184,33 @@ int mla_decode_latent_fp8(const uint16_t* q_lat, const uint16_t* q_pe, const uin
  * 128), enough work units for every CU with chunks of at least 256 entries.
  * The split partial buffers of mla_decode_sparse hold B*T*S rows. */
 int mla_sparse_split_count(int B, int T, int H, int topk, int num_splits, int* splits);
+
+/* mla_decode_latent without caller scratch, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments and results are those of
+ * mla_decode_latent with out_latent required (the merged result is written);
+ * the automatic plan's work list, split_indptr and the split partials (bf16,
+ * with their f32 lse) live in a device array of 64 MiB that the library holds
+ * on every GPU it runs on until the process ends.  No allocation and no
+ * allocating library routine is called; the first call on a device resolves
+ * that device's array address (hipGetSymbolAddress) and keeps it.
+ *   num_splits  1: as mla_decode_latent (no scratch); S > 1 or 0 (automatic):
+ *               split decode + merge through the array.
+ * Limit: the plan (256 + 16 * rows bytes), split table (4 * (B + 1)), partial
+ * lse (4 * rows * T * H) and bf16 partials (1024 * rows * T * H), each rounded
+ * up to 256 bytes, must fit in 64 MiB, rows = max_total_splits of
+ * mla_decode_workspace_size for the same arguments (on the headline geometry,
+ * B = 64, H = 128, the automatic mode needs 42 MB); beyond it the call returns
+ * MLA_ERR_WORKSPACE and enqueues nothing.  MLA_ERR_DEVICE if the current device
+ * cannot be queried.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams or host threads) race
+ * on it and must be serialised by the caller. */
+int mla_decode_latent_noalloc(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                              int num_blocks, int page_size, const int32_t* block_table, int max_blocks_per_seq,
+                              const int32_t* seqlens, int B, int T, int H, int r, int d_R, int max_seqlen,
+                              float softmax_scale, int num_splits, void* out_latent, mla_dtype out_dtype,
+                              float* lse, void* stream);
 
 /* Sparse (top-k) absorbed latent attention.  Query token (b, t) -- all H heads
  * -- attends to the cache rows listed in its index row, without a causal mask:

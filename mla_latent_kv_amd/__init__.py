@@ -66,6 +66,7 @@ def load_library():
     L.mla_decode_latent.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I,
                                     P, SZ, P, I, P, P, P, I, P, P]
     L.mla_decode_latent_fp8.argtypes = L.mla_decode_latent.argtypes
+    L.mla_decode_latent_noalloc.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I, P, I, P, P]
     L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
@@ -74,7 +75,8 @@ def load_library():
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
-                 "mla_decode_sparse", "mla_validate_inputs", "mla_decode_latent_fp8"):
+                 "mla_decode_sparse", "mla_validate_inputs", "mla_decode_latent_fp8",
+                 "mla_decode_latent_noalloc"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -295,6 +297,44 @@ def _decode(fp8, q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softma
     return (out_latent, lse) if want_out else (None, None)
 
 
+def mla_decode_latent_noalloc(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale,
+                              num_splits=0, out_latent=None, lse=None, out_dtype=None, stream=None):
+    """mla_decode_latent with its split scratch in the library's own device
+    array (the C entry point allocates nothing; see include/mla_latent.h).
+    Pass ``out_latent`` and ``lse`` to make the whole call allocation-free;
+    otherwise they are allocated here with torch.  Returns (out_latent, lse)."""
+    torch = _torch()
+    what = "mla_decode_latent_noalloc"
+    _need(q_lat, (torch.bfloat16,), what + " q_lat")
+    _need(q_pe, (torch.bfloat16,), what + " q_pe")
+    _need(kv_cache, (torch.bfloat16,), what + " kv_cache")
+    _need(block_table, (torch.int32,), what + " block_table")
+    _need(seqlens, (torch.int32,), what + " seqlens")
+    _need(lse, (torch.float32,), what + " lse")
+    B, T, H, r = q_lat.shape
+    dr = q_pe.shape[3]
+    num_blocks, page_size, _ = kv_cache.shape
+    _shape(q_pe, (B, T, H, dr), what + " q_pe")
+    _shape(kv_cache, (num_blocks, page_size, r + dr), what + " kv_cache")
+    if block_table.dim() != 2 or block_table.shape[0] < B or seqlens.dim() != 1 or seqlens.shape[0] < B:
+        raise ValueError(what + ": block_table [>=B, max_blocks] and seqlens [>=B] expected")
+    _shape(out_latent, (B, T, H, r), what + " out_latent")
+    _shape(lse, (B, T, H), what + " lse")
+    if out_dtype is None:
+        out_dtype = out_latent.dtype if out_latent is not None else torch.bfloat16
+    elif out_latent is not None and out_latent.dtype != out_dtype:
+        raise ValueError("out_latent's dtype differs from out_dtype")
+    if out_latent is None:
+        out_latent = torch.empty((B, T, H, r), dtype=out_dtype, device=q_lat.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q_lat.device)
+    _check(load_library().mla_decode_latent_noalloc(
+        _ptr(q_lat), _ptr(q_pe), _ptr(kv_cache), num_blocks, page_size, _ptr(block_table), block_table.shape[1],
+        _ptr(seqlens), B, T, H, r, dr, int(max_seqlen), float(softmax_scale), int(num_splits), _ptr(out_latent),
+        _dtype_code(out_dtype), _ptr(lse), _stream(stream)), what)
+    return out_latent, lse
+
+
 def mla_merge_splits(part_out, part_lse, split_indptr, B, out_latent=None, lse=None,
                      out_dtype=None, stream=None):
     """Merge partials -> (out_latent [B,T,H,512], lse [B,T,H])."""
@@ -513,7 +553,8 @@ def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, ma
 
 __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "load_normal_library", "status_string", "mla_status_string",
-    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
+    "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8",
+    "mla_decode_latent_noalloc", "mla_merge_splits",
     "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
     "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",

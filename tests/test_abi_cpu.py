@@ -69,9 +69,11 @@ def test_decode_library_links_no_rocblas(lib):
 
 def test_decode_library_keeps_no_state(lib):
     """No writable data of the library's own: the only writable symbols are the
-    toolchain's (ELF bookkeeping, the HIP fat-binary registration handles) and
-    the host-side handles of the kernels.  A rocBLAS handle table, a mutex or a
-    cached plan would show up here."""
+    toolchain's (ELF bookkeeping, the HIP fat-binary registration handles), the
+    host-side handles of the kernels, and the no-allocation entry point's
+    device array (its host-side stand-in), per-device address table and their
+    mutex.  A rocBLAS handle table, another mutex or a cached plan would show
+    up here."""
     syms = _elf(["nm", "-C", "--defined-only"], mk.LIB_PATH).splitlines()
     own = []
     for line in syms:
@@ -83,8 +85,65 @@ def test_decode_library_keeps_no_state(lib):
             continue
         if re.fullmatch(r"mla::\w+_kernel(<.*>)?\(.*\)", name):   # kernel launch handles
             continue
+        if name in NOALLOC_STATE:
+            continue
         own.append(name)
     assert not own, own
+
+
+NOALLOC_STATE = {"(anonymous namespace)::noalloc_scratch", "(anonymous namespace)::g_noalloc_ptr",
+                 "(anonymous namespace)::g_noalloc_mu"}
+
+
+def _file_scope_variables(src):
+    """Declarations at namespace scope that are neither functions nor
+    constants (a crude C++ scan: comments stripped, braces counted)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"^\s*#.*$", "", src, flags=re.M)
+    depth, top, line = 0, [], ""
+    scopes = []   # True for a namespace / extern "C" brace
+    for ch in src:
+        if ch == "{":
+            head = " ".join(line.split())
+            is_ns = head.startswith(("namespace", 'extern "C"')) and "(" not in head
+            if all(scopes) and not is_ns:
+                top.append(head)
+            scopes.append(is_ns)
+            line = ""
+        elif ch == "}":
+            scopes.pop()
+            line = ""
+        elif ch == ";":
+            if all(scopes):
+                top.append(" ".join(line.split()))
+            line = ""
+        else:
+            line += ch
+    out = []
+    for d in top:
+        if not d or "(" in d or d.startswith(("constexpr", "using", "typedef", "struct", "class", "enum",
+                                               "template", "static_assert", "return")):
+            continue
+        if re.match(r"^(static\s+)?(const\s+)?[\w:<>,\*&\s]+\s+[\w\[\]\d]+\s*(=.*)?$", d) and \
+                not re.match(r"^(static\s+)?const\s", d):
+            out.append(d)
+    return out
+
+
+def test_file_scope_scan_flags_mutable_globals():
+    """The scan below catches the kinds of state this library must not hold."""
+    bad = """namespace { std::mutex g_mu; rocblas_handle g_blas[64] = {}; int counter = 0;
+             constexpr int kX = 4; int f(int a) { int local = a; return local; } }
+             extern "C" { int mla_x(void) { static int calls; return calls; } }"""
+    assert _file_scope_variables(bad) == ["std::mutex g_mu", "rocblas_handle g_blas[64] =", "int counter = 0"]
+
+
+def test_api_source_has_no_file_scope_state():
+    """The ABI source itself (api.cpp: validation, sizing, launches) declares no
+    file-scope variable other than constants."""
+    src = open(os.path.join(ROOT, "mla_latent_kv_amd", "csrc", "api.cpp")).read()
+    assert _file_scope_variables(src) == []
 
 
 def test_status_strings(lib):
@@ -426,3 +485,19 @@ def test_binding_rejects_sparse_buffers_of_another_call(lib):
     ok = mk.SparseBuffers(B, T, H, topk, 4, "cpu")
     with pytest.raises(ValueError, match="device"):
         mk.mla_decode_sparse(q, qp, kv, idx, None, 0.07, num_splits=4, buffers=ok)
+
+
+def test_noalloc_rejects_what_exceeds_its_array(lib):
+    """mla_decode_latent_noalloc refuses, before any device call, a split whose
+    scratch would not fit in its 64 MiB array, and needs an output."""
+    f = lib.mla_decode_latent_noalloc
+
+    def call(B, T, H, maxL, S, out=P16):
+        return f(P16, P16, P16, 1 << 14, 64, P16, (maxL + 63) // 64, P16, B, T, H, 512, 64, maxL,
+                 ctypes.c_float(0.07), S, out, 0, None, None)
+    # 64 sequences x 64 splits x 8 x 128 query rows of bf16 partials: 4 GiB
+    assert call(64, 8, 128, 8192, 64) == WS
+    # 128 rows x 512 splits of one sequence: 64 MiB of partials plus the rest
+    assert call(1, 1, 128, 1 << 20, 512) == WS
+    assert call(2, 1, 128, 4096, 4, out=None) == NULL
+    assert call(0, 1, 128, 4096, 4) == OK             # empty batch: nothing to do
