@@ -464,13 +464,16 @@ def power_roof(seconds, dev):
     lib.mla_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     grid, slice_ = 256, 4 << 20
-    src = torch.ones(grid * slice_, dtype=torch.uint8, device=dev)
+    # random bf16 N(0,1) values: the LDS-fed modes then multiply changing data, as the decode does
+    src = torch.randn(grid * slice_ // 2, dtype=torch.float32, device=dev).to(torch.bfloat16).view(torch.uint8)
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     out = []
-    for name, mode, ratio, iters in (("mfma_only", 0, 7, 16000), ("hbm_stream_only", 1, 7, 6000),
-                                     ("mfma_and_stream_224_flop_per_byte", 2, 7, 10000),
-                                     ("mfma_stream_and_lds_reads_224_flop_per_byte", 3, 7, 10000)):
+    for name, mode, ratio, iters in (("mfma_only_constant_operands", 0, 7, 16000),
+                                     ("mfma_lds_fed_random_operands", 4, 7, 16000),
+                                     ("hbm_stream_only", 1, 7, 6000),
+                                     ("mfma_constant_operands_and_stream_224_flop_per_byte", 2, 7, 10000),
+                                     ("mfma_lds_fed_random_operands_and_stream_224_flop_per_byte", 3, 7, 10000)):
         def launch():
             st = lib.mla_probe_launch(ctypes.c_void_p(src.data_ptr()), slice_, grid, iters, mode, ratio,
                                       ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
@@ -498,7 +501,7 @@ def power_roof(seconds, dev):
         ms = float(np.median([a.elapsed_time(b) for a, b in evs[1:]])) / 8
         waves = grid * 4
         flops = waves * 4 * iters * 32768 if mode != 1 else 0
-        loads = iters if mode == 1 else (4 * iters) // ratio if mode >= 2 else 0
+        loads = iters if mode == 1 else (4 * iters) // ratio if mode in (2, 3) else 0
         nbytes = waves * loads * 1024
         summ = sampler.summary(t0 + 0.3, t1 - 0.05, ["current_gfxclks_mean", "current_socket_power"])
         clk = summ.get("current_gfxclks_mean", {}).get("median")

@@ -10,7 +10,12 @@
 //           (floor(4 iters / ratio) loads: 32768 * ratio / 1024 FLOP per byte);
 //   mode 3  as mode 2, plus one 16-byte-per-lane LDS read (1 KB per wave)
 //           feeding each MFMA's B operand, read one group ahead (about the
-//           decode kernel's LDS operand traffic per MFMA).
+//           decode kernel's LDS operand traffic per MFMA);
+//   mode 4  the MFMAs with their LDS operand reads, no HBM stream.
+// In modes 3 and 4 each wave first fills its 32 KB LDS window from `src`, so
+// with random data in `src` the MFMA operands change from one instruction to
+// the next as they do in the decode kernel (the matrix cores draw more power
+// on toggling operands than on constant ones, modes 0 and 2).
 // Workgroup g streams its own slice [g * slice, (g + 1) * slice) of `src`
 // (at most 24 loads in flight per wave).  The work per launch is known
 // exactly, so rate = work / duration; a long run of launches, sampled for
@@ -20,7 +25,7 @@
 // extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters,
 //                                 int mode, int ratio, float* sink, void* stream)
 //   src: device buffer of at least grid * slice bytes, slice a multiple of 4 KB
-//   and at least 4 KB; iters even; ratio 1..64; sink: 256 floats (never
+//   and at least 32 KB; mode 0..4; iters even; ratio 1..64; sink: 256 floats (never
 //   written for these inputs; keeps the results live).  Returns a hipError_t.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -78,6 +83,10 @@ __global__ __launch_bounds__(256, 1) void roof_kernel(const uint8_t* src, size_t
   auto rd16 = [&](uint32_t off) {
     return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(win + (off & 32767u) + 16u * (uint32_t)l);
   };
+  if (mode >= 3) {   // fill this wave's window with 32 KB of `src`
+    for (int k = 0; k < 32; ++k) load();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   if (mode == 0) {
     for (int i = 0; i < iters; ++i) group(y, y, y, y);
   } else if (mode == 1) {
@@ -88,7 +97,9 @@ __global__ __launch_bounds__(256, 1) void roof_kernel(const uint8_t* src, size_t
       loads_due();
     }
   } else {
-    // two groups per iteration: group A uses ya (while yb is read), group B yb
+    // two groups per iteration: group A uses ya (while yb is read), group B yb;
+    // mode 4 issues no loads (ratio is ignored)
+    if (mode == 4) ratio = 1 << 30;
     uint32_t off = 0;
     bf16x8 ya0 = rd16(off), ya1 = rd16(off + 1024), ya2 = rd16(off + 2048), ya3 = rd16(off + 3072);
     off += 4096;
@@ -115,8 +126,8 @@ __global__ __launch_bounds__(256, 1) void roof_kernel(const uint8_t* src, size_t
 
 extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters, int mode, int ratio,
                                 float* sink, void* stream) {
-  if (!src || !sink || grid < 1 || iters < 2 || iters % 2 || mode < 0 || mode > 3 || ratio < 1 || ratio > 64 ||
-      slice < 4096 || slice % 4096)
+  if (!src || !sink || grid < 1 || iters < 2 || iters % 2 || mode < 0 || mode > 4 || ratio < 1 || ratio > 64 ||
+      slice < 32768 || slice % 4096)
     return (int)hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)roof_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (e != hipSuccess) return (int)e;
