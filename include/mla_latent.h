@@ -22,7 +22,8 @@
  *
  * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
  * written at their paged positions before the decode that reads them); for
- * sparse (top-k) attention, mla_decode_sparse in place of mla_decode_latent.
+ * sparse (top-k) attention, mla_decode_sparse (bf16 rows) and
+ * mla_decode_sparse_fp8 (FP8 rows) in place of mla_decode_latent.
  * The same function in the Normal (per-head up-projected) association order,
  * for comparison, is a separate library: mla_normal.h / libmla_normal.so.
  *
@@ -241,6 +242,21 @@ int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
                       float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
                       float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
                       float* lse, void* stream);
+
+/* mla_decode_sparse over a pool of FP8 rows (the row layout of
+ * mla_decode_latent_fp8: 512 E4M3 codes, four fp32 scales, 64 bf16 rope
+ * values; 656 bytes, kv_cache 16-byte aligned): every argument and result as
+ * for mla_decode_sparse, the selected rows dequantized to bf16 in the kernel
+ * as mla_decode_latent_fp8 does (c = bf16(code * scale), nearest even).
+ * Source: M5.8 0x0B ("Exact 656-byte FP8 row"; sparse indices are physical
+ * execution metadata) and 0x08 (the checked sparse decode path reads the FP8
+ * cache). */
+int mla_decode_sparse_fp8(const uint16_t* q_lat, const uint16_t* q_pe, const uint8_t* kv_cache,
+                          int num_blocks, int page_size, const int32_t* indices, int topk,
+                          const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                          float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                          float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                          float* lse, void* stream);
 
 /* Merge of split partial states, per (b,t,h) over rows k in
  * [split_indptr[b], split_indptr[b+1]):  M = max_k lse_k, w_k = exp(lse_k - M),

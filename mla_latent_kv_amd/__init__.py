@@ -72,11 +72,12 @@ def load_library():
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
     L.mla_sparse_split_count.argtypes = [I, I, I, I, I, P]
     L.mla_decode_sparse.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, F, I, P, I, P, P, P, I, P, P]
+    L.mla_decode_sparse_fp8.argtypes = L.mla_decode_sparse.argtypes
     L.mla_validate_inputs.argtypes = [P, I, P, I, I, I, I, I, P]
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
                  "mla_decode_sparse", "mla_validate_inputs", "mla_decode_latent_fp8",
-                 "mla_decode_latent_noalloc"):
+                 "mla_decode_latent_noalloc", "mla_decode_sparse_fp8"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -427,10 +428,24 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     indices [B,T,topk] int32 physical rows, topk_length [B] int32 or None.
     Returns (out_latent, lse); with more than one split and merge=False the
     partials stay in ``buffers`` and (None, None) is returned."""
+    return _sparse(False, q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale, num_splits, out_dtype,
+                   buffers, out_latent, lse, merge, stream)
+
+
+def mla_decode_sparse_fp8(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale, num_splits=0,
+                          out_dtype=None, buffers: Optional[SparseBuffers] = None, out_latent=None, lse=None,
+                          merge=True, stream=None):
+    """mla_decode_sparse over FP8 rows: ``kv_cache`` is uint8 [num_blocks, P, 656]."""
+    return _sparse(True, q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale, num_splits, out_dtype,
+                   buffers, out_latent, lse, merge, stream)
+
+
+def _sparse(fp8, q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale, num_splits, out_dtype, buffers,
+            out_latent, lse, merge, stream):
     torch = _torch()
     _need(q_lat, (torch.bfloat16,), "mla_decode_sparse q_lat")
     _need(q_pe, (torch.bfloat16,), "mla_decode_sparse q_pe")
-    _need(kv_cache, (torch.bfloat16,), "mla_decode_sparse kv_cache")
+    _need(kv_cache, (torch.uint8,) if fp8 else (torch.bfloat16,), "mla_decode_sparse kv_cache")
     _need(indices, (torch.int32,), "mla_decode_sparse indices")
     _need(topk_length, (torch.int32,), "mla_decode_sparse topk_length")
     B, T, H, r = q_lat.shape
@@ -440,7 +455,7 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     if tuple(indices.shape[:2]) != (B, T) or (topk_length is not None and topk_length.shape[0] < B):
         raise ValueError("mla_decode_sparse: indices / topk_length do not match q_lat")
     _shape(q_pe, (B, T, H, dr), "mla_decode_sparse q_pe")
-    _shape(kv_cache, (num_blocks, page_size, r + dr), "mla_decode_sparse kv_cache")
+    _shape(kv_cache, (num_blocks, page_size, 656 if fp8 else r + dr), "mla_decode_sparse kv_cache")
     _shape(out_latent, (B, T, H, r), "mla_decode_sparse out_latent")
     _shape(lse, (B, T, H), "mla_decode_sparse lse")
     if out_dtype is None:
@@ -468,14 +483,15 @@ def mla_decode_sparse(q_lat, q_pe, kv_cache, indices, topk_length, softmax_scale
     if want_out and lse is None:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=q_lat.device)
     split = S != 1
-    _check(load_library().mla_decode_sparse(
+    lib = load_library()
+    _check((lib.mla_decode_sparse_fp8 if fp8 else lib.mla_decode_sparse)(
         _ptr(q_lat), _ptr(q_pe), _ptr(kv_cache), num_blocks, page_size, _ptr(indices), topk,
         _ptr(topk_length), B, T, H, r, dr, float(softmax_scale), S,
         _ptr(buffers.part_out if split else None),
         _dtype_code(buffers.part_out.dtype) if split else MLA_F32,
         _ptr(buffers.part_lse if split else None), _ptr(buffers.split_indptr if split else None),
         _ptr(out_latent if want_out else None), _dtype_code(out_dtype),
-        _ptr(lse if want_out else None), _stream(stream)), "mla_decode_sparse")
+        _ptr(lse if want_out else None), _stream(stream)), "mla_decode_sparse_fp8" if fp8 else "mla_decode_sparse")
     return (out_latent, lse) if want_out else (None, None)
 
 
@@ -555,7 +571,8 @@ __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "load_normal_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8",
     "mla_decode_latent_noalloc", "mla_merge_splits",
-    "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "SparseBuffers",
+    "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "mla_decode_sparse_fp8",
+    "SparseBuffers",
     "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",
 ]

@@ -272,12 +272,13 @@ int mla_sparse_split_count(int B, int T, int H, int topk, int num_splits, int* s
   return MLA_OK;
 }
 
-int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
-                      int num_blocks, int page_size, const int32_t* indices, int topk,
-                      const int32_t* topk_length, int B, int T, int H, int r, int d_R,
-                      float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
-                      float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
-                      float* lse, void* stream) {
+// sparse decode over bf16 rows (fp8 false) or FP8 rows (fp8 true)
+static int sparse_impl(const uint16_t* q_lat, const uint16_t* q_pe, const void* kv_cache, bool fp8,
+                       int num_blocks, int page_size, const int32_t* indices, int topk,
+                       const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                       float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                       float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                       float* lse, void* stream) {
   if (B < 0 || num_blocks < 1 || topk < 1 || num_splits < 0) return MLA_ERR_SHAPE;
   int st = check_heads(T, H);
   if (st) return st;
@@ -321,7 +322,7 @@ int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
     p.out = out_latent;
     p.lse = lse;
     p.n_units = (int)(BT * n_rg);
-    return launch_status(mla::launch_decode(p, p.n_units, false, out_dtype == MLA_F32, s, true));
+    return launch_status(mla::launch_decode(p, p.n_units, false, out_dtype == MLA_F32, s, true, fp8));
   }
   if (!part_out || !part_lse || !split_indptr) return MLA_ERR_WORKSPACE;
   if (!aligned16(part_out) || !aligned4(part_lse) || !aligned4(split_indptr)) return MLA_ERR_ALIGN;
@@ -332,12 +333,34 @@ int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_
   p.num_splits = S;
   p.n_units = (int)(BT * S * n_rg);
   const bool part_f32 = part_dtype == MLA_F32;
-  if ((st = launch_status(mla::launch_decode(p, p.n_units, true, part_f32, s, true)))) return st;
+  if ((st = launch_status(mla::launch_decode(p, p.n_units, true, part_f32, s, true, fp8)))) return st;
   if (out_latent) {
     mla::MergeParams mp{part_out, part_lse, split_indptr, (int)BT, H, out_latent, lse};
     return launch_status(mla::launch_merge(mp, part_f32, out_dtype == MLA_F32, s));
   }
   return MLA_OK;
+}
+
+int mla_decode_sparse(const uint16_t* q_lat, const uint16_t* q_pe, const uint16_t* kv_cache,
+                      int num_blocks, int page_size, const int32_t* indices, int topk,
+                      const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                      float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                      float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                      float* lse, void* stream) {
+  return sparse_impl(q_lat, q_pe, kv_cache, false, num_blocks, page_size, indices, topk, topk_length, B, T, H, r,
+                     d_R, softmax_scale, num_splits, part_out, part_dtype, part_lse, split_indptr, out_latent,
+                     out_dtype, lse, stream);
+}
+
+int mla_decode_sparse_fp8(const uint16_t* q_lat, const uint16_t* q_pe, const uint8_t* kv_cache,
+                          int num_blocks, int page_size, const int32_t* indices, int topk,
+                          const int32_t* topk_length, int B, int T, int H, int r, int d_R,
+                          float softmax_scale, int num_splits, void* part_out, mla_dtype part_dtype,
+                          float* part_lse, int32_t* split_indptr, void* out_latent, mla_dtype out_dtype,
+                          float* lse, void* stream) {
+  return sparse_impl(q_lat, q_pe, kv_cache, true, num_blocks, page_size, indices, topk, topk_length, B, T, H, r,
+                     d_R, softmax_scale, num_splits, part_out, part_dtype, part_lse, split_indptr, out_latent,
+                     out_dtype, lse, stream);
 }
 
 int mla_append_cache(const uint16_t* c_new, const uint16_t* kpe_new, uint16_t* kv_cache, int num_blocks,

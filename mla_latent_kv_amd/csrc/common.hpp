@@ -106,6 +106,12 @@ __device__ __forceinline__ void dma4s(uint32_t voff, const void* base, uint32_t 
                : "memory");
 }
 
+// 4 bytes per lane from a 64-bit per-lane address into LDS at lds_addr + 4 * lane.
+__device__ __forceinline__ void dma4v(const void* addr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds_addr)
+               : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

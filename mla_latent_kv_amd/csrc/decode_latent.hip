@@ -241,7 +241,6 @@ __device__ __forceinline__ int unit_keys(const DecodeParams& p, int bb) {
 
 template <int NB, bool SPLIT, bool OUT_F32, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
-  static_assert(!(SPARSE && FP8), "the sparse path reads bf16 rows");
   static_assert(!FP8 || NB == 3, "FP8 ring: the tiles of steps i, i+1 and the one being converted");
   constexpr int kRB = FP8 ? kF8Row : kRowBytes;  // bytes per cached row
   // step ring (FP8: followed by two code staging buffers); after the last step
@@ -251,6 +250,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kRingBytes];
   // probabilities of all 128 rows, two steps: [step & 1][kb][row block][lane] x 16 B
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * 2 * 4 * 64 * 16];
+  // FP8 rows selected by index: the row ids of this wave's half for four
+  // steps, [wave][step & 3][16] int32 (1 KB of the 2 KB the FP8 ring leaves)
+  __shared__ __attribute__((aligned(16))) int f8_idbuf[SPARSE && FP8 ? 4 * 4 * 16 : 1];
 
   const int w = wave_id();
   const int l = lane_id();
@@ -341,6 +343,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   const uint32_t dma_voff = ((l & 15) ^ tile_swz(l >> 4)) * kRowBytes + 16 * (l >> 4) + 64 * (w & 1);
   const int rsw = (l & 15) ^ tile_swz(l >> 4);  // sparse: row of the half this lane loads
   const uint32_t dma_coff = 16 * (l >> 4) + 64 * (w & 1);
+  // FP8 rows selected by index: the rows of the half whose codes, scales and
+  // rope values this lane loads (the lane layout of the FP8 loads below)
+  const int f8_rc = l & 15, f8_rs = l >> 2, f8_rr = (l & 15) ^ tile_swz(l >> 4);
   // FP8 rows, per wave and step: the rope values of its half's 16 rows straight
   // into the tile (lane l: rope chunk 4 pw + (l >> 4) of row (l & 15) ^ g(l >> 4),
   // i.e. tile chunk 64 + 4 pw + (l >> 4)); four 1 KB code blocks into the
@@ -386,10 +391,38 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // later step's 32 ids arrive by a direct-to-LDS load issued NB steps ahead
   // into this wave's quarter of the idle probability buffer (see the step body).
   const int32_t* const idx_row = SPARSE ? p.indices + (size_t)b * p.topk : nullptr;
-  auto idx_of = [&](int it) { return min(j0 + kStepTok * it + 16 * hw + rsw, p.topk - 1); };
+  auto idx_at = [&](int it, int r) { return min(j0 + kStepTok * it + 16 * hw + r, p.topk - 1); };
+  auto idx_of = [&](int it) { return idx_at(it, rsw); };
+  // Steps whose row ids are loaded before the loop; during step i the ids of
+  // step i + kIdsAhead arrive (FP8: one step more, the codes are loaded three
+  // steps ahead).  FP8 keeps three ids per lane and step: the rows of its code,
+  // scale and rope loads.
+  constexpr int kIdsAhead = FP8 ? NB + 1 : NB;
   int sidx_pro[NB];
   int sidx = 0;  // row id of this lane for the next step to issue
-  if constexpr (SPARSE) {
+  // FP8 sparse: the ids of step k sit in slot k & 3 of this wave's part of
+  // f8_idbuf (16 ids of its half); the first steps' ids are written by the
+  // lanes below, later ones by a direct-to-LDS load four steps ahead.
+  // f8c / f8s / f8r: the code, scale and rope row ids of this lane, read back
+  // from the slots for the step about to be issued (f8r: its rope step)
+  const uint32_t f8_ids_lds = lds_addr_of(f8_idbuf) + w * 256;
+  int f8c = 0, f8s = 0, f8r = 0;
+  auto f8_id_at = [&](int k, int r) {
+    return *(const __attribute__((address_space(3))) int*)(uintptr_t)(f8_ids_lds + 64 * (k & 3) + 4 * r);
+  };
+  auto f8_load_ids = [&]() {
+    // lanes 0-15 write the ids of the first kIdsAhead steps (visible to this
+    // wave's own reads after its next LDS wait)
+    if (l < 16) {
+#pragma unroll
+      for (int it = 0; it < kIdsAhead; ++it)
+        *(__attribute__((address_space(3))) int*)(uintptr_t)(f8_ids_lds + 64 * (it & 3) + 4 * l) =
+            idx_row[idx_at(it, l)];
+    }
+  };
+  if constexpr (SPARSE && FP8) {
+    f8_load_ids();
+  } else if constexpr (SPARSE) {
 #pragma unroll
     for (int it = 0; it < NB; ++it) sidx_pro[it] = idx_row[idx_of(it)];
   } else {
@@ -407,7 +440,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   for (int ks = 0; ks < kDR / 16; ++ks) q[kR / 16 + ks] = *(const bf16x8*)(qp + 16 * ks);
   // consume the page ids here: the compiler's wait for them then counts the
   // query loads behind them exactly
-  if constexpr (SPARSE) {
+  if constexpr (SPARSE && FP8) {
+    wait_lgkm0();   // the first steps' ids are in LDS
+  } else if constexpr (SPARSE) {
 #pragma unroll
     for (int it = 0; it < NB; ++it) asm volatile("" ::"v"(sidx_pro[it]));
   } else {
@@ -419,6 +454,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 
   const uint8_t* dma_base = cache;
   const uint8_t* dma_vaddr = cache;  // sparse: this lane's row + dma_coff
+  const uint8_t* f8_code_va = cache;   // FP8 sparse: this lane's code row + its column offset
+  bool f8_live_c = false, f8_live_r = false;   // FP8 sparse: the half of the code / rope step is in range
+  // FP8 sparse: row of this lane's load (rows past the range read rows 0-15 of
+  // the pool, like the dense path)
+  auto f8_row = [&](bool live, int id, int dead) {
+    return live ? min((uint32_t)id, p.num_rows - 1u) : (uint32_t)dead;
+  };
   uint32_t dma_dst = 0;
   const uint32_t stg_lds = tiles_lds + NB * kStepBytes;  // FP8 code staging (two steps)
   uint32_t f8_scale_dst = 0;
@@ -437,7 +479,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     } else {
       dma_dst = tiles_lds + (it % NB) * kStepBytes + hw * kTileBytes + 1024 * (w & 1);
     }
-    if constexpr (SPARSE) {
+    if constexpr (SPARSE && FP8) {
+      f8_live_c = half_live(it);   // (the addresses are formed at each load: short live ranges)
+      return;
+    } else if constexpr (SPARSE) {
       const uint32_t row = half_live(it) ? min((uint32_t)sidx, p.num_rows - 1u) : (uint32_t)rsw;
       dma_vaddr = cache + (uint64_t)row * kRowBytes + dma_coff;
       return;
@@ -466,12 +511,27 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // the ring), 1-4 the codes and 5 the scales (rows dma_base into staging)
   auto f8_issue_part = [&](auto n_const) {
     constexpr int n = decltype(n_const)::value;
-    if constexpr (n == 0) dma16s(f8_rope_voff, f8_rope_base, f8_rope_dst);
-    else if constexpr (n <= 4) dma16s_imm<64 * (n - 1)>(f8_code_voff, dma_base, dma_dst + 1024 * (n - 1));
-    else dma4s(f8_scale_voff, dma_base, f8_scale_dst);
+    if constexpr (SPARSE) {
+      if constexpr (n == 0) {
+        dma16v<0>(cache + (uint64_t)f8_row(f8_live_r, f8r, f8_rr) * kF8Row + (kF8Rope + 64 * pw + 16 * (l >> 4)),
+                  f8_rope_dst);
+      } else if constexpr (n <= 4) {
+        if constexpr (n == 1)
+          f8_code_va = cache + (uint64_t)f8_row(f8_live_c, f8c, f8_rc) * kF8Row + (256 * pw + 16 * (l >> 4));
+        dma16v<64 * (n - 1)>(f8_code_va, dma_dst + 1024 * (n - 1));
+      } else {
+        dma4v(cache + (uint64_t)f8_row(f8_live_c, f8s, f8_rs) * kF8Row + (kF8Scales + 4 * (l & 3)), f8_scale_dst);
+      }
+    } else {
+      if constexpr (n == 0) dma16s(f8_rope_voff, f8_rope_base, f8_rope_dst);
+      else if constexpr (n <= 4) dma16s_imm<64 * (n - 1)>(f8_code_voff, dma_base, dma_dst + 1024 * (n - 1));
+      else dma4s(f8_scale_voff, dma_base, f8_scale_dst);
+    }
   };
-  // tile k's rope values come from the rows of the codes prepared last
+  // tile k's rope values come from the rows of the codes prepared last (sparse:
+  // from rope row id rid of tile k)
   auto f8_rope_prep = [&](int k) {
+    if constexpr (SPARSE) f8_live_r = half_live(k);
     f8_rope_base = dma_base;
     f8_rope_dst = tiles_lds + (k % NB) * kStepBytes + hw * kTileBytes + (kTileBytes - 2048) + 1024 * pw;
   };
@@ -486,25 +546,37 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // swizzles of c & 3 = 2a and 2a + 1 differ by 12 for either a).
   const uint32_t f8_rl = 16 * l;
   const uint32_t f8_wl = 512 * (l >> 4) + 16 * ((l & 15) ^ tile_swz(2 * ((l >> 4) & 1)));
-  auto f8_read = [&](int k, auto n_const) {
-    constexpr int n = decltype(n_const)::value;
+  // Per-tile LDS bases of the conversion (staging reads, scale reads and the
+  // two lane patterns of the tile writes), recomputed for each tile and hidden
+  // behind opaque() so that every access is base + immediate: precomputed per
+  // (buffer, unit, half) the addresses outnumber the free registers and were
+  // spilled, and each reload then waited for every tile load in flight.
+  uint32_t f8_rb = 0, f8_sb = 0, f8_wb0 = 0, f8_wb1 = 0;
+  auto f8_bases = [&](int k) {
     const uint32_t sb = stg_lds + (k & 1) * kStgBytes;
-    f8_raw = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(sb + hw * 8192 + pw * 4096 + 1024 * n + f8_rl);
-    f8_sc = *(const __attribute__((address_space(3))) float*)(uintptr_t)(sb + kStgCodes + w * 256 + 4 * (2 * pw + (n >> 1)) +
-                                                                     (f8_rl & 0xF0u));
+    f8_rb = opaque(sb + hw * 8192 + pw * 4096 + f8_rl);
+    f8_sb = opaque(sb + kStgCodes + w * 256 + 8 * pw + (f8_rl & 0xF0u));
+    const uint32_t tb = tiles_lds + (k % NB) * kStepBytes + hw * kTileBytes + 8192 * pw;
+    f8_wb0 = opaque(tb + f8_wl);
+    f8_wb1 = opaque(tb + (f8_wl ^ 192u));
   };
-  auto f8_write = [&](int k, auto n_const, auto e_const) {
+  auto f8_read = [&](auto n_const) {
+    constexpr int n = decltype(n_const)::value;
+    f8_raw = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(f8_rb + 1024 * n);
+    f8_sc = *(const __attribute__((address_space(3))) float*)(uintptr_t)(f8_sb + 4 * (n >> 1));
+  };
+  auto f8_write = [&](auto n_const, auto e_const) {
     constexpr int n = decltype(n_const)::value, e = decltype(e_const)::value;
     const u32x2 v0 = f8x4_to_bf16(f8_raw[2 * e], f8_sc), v1 = f8x4_to_bf16(f8_raw[2 * e + 1], f8_sc);
-    const uint32_t lane = e ? (f8_wl ^ 192u) : f8_wl;
-    const uint32_t dst = tiles_lds + (k % NB) * kStepBytes + hw * kTileBytes + 512 * (16 * pw + 4 * n) + 256 * e + lane;
+    const uint32_t dst = (e ? f8_wb1 : f8_wb0) + 2048 * n + 256 * e;
     *(__attribute__((address_space(3))) u32x4*)(uintptr_t)dst = u32x4{v0[0], v0[1], v1[0], v1[1]};
   };
   auto f8_convert = [&](int k) {  // the whole tile, not interleaved (prologue)
+    f8_bases(k);
     static_for<0, 4>([&](auto n) {
-      f8_read(k, n);
-      f8_write(k, n, std::integral_constant<int, 0>{});
-      f8_write(k, n, std::integral_constant<int, 1>{});
+      f8_read(n);
+      f8_write(n, std::integral_constant<int, 0>{});
+      f8_write(n, std::integral_constant<int, 1>{});
     });
   };
   auto f8_issue_codes = [&]() {
@@ -522,8 +594,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   const uint32_t ids_lds0 = lds_addr_of(pbuf) + w * kPbufRowBlock;  // token block 0, row block w
   auto ids_lds = [&](int i) { return ids_lds0 + ((i + 1) & 1) * kPbufParity; };
   auto idx_dma = [&](int i) {
-    const uint32_t voff = 4u * (uint32_t)min(j0 + kStepTok * (i + NB) + (l & 31), p.topk - 1);
-    dma4s(voff, idx_row, ids_lds(i));
+    if constexpr (FP8) {
+      // the ids of this wave's half of step i + 4, lanes 0-15 only (64 bytes)
+      if (l < 16) {
+        const uint32_t voff = 4u * (uint32_t)min(j0 + kStepTok * (i + kIdsAhead) + 16 * hw + l, p.topk - 1);
+        dma4s(voff, idx_row, f8_ids_lds + 64 * ((i + kIdsAhead) & 3));
+      }
+    } else {
+      const uint32_t voff = 4u * (uint32_t)min(j0 + kStepTok * (i + kIdsAhead) + (l & 31), p.topk - 1);
+      dma4s(voff, idx_row, ids_lds(i));
+    }
   };
   auto issue = [&](int it) {
     issue_prep(it);
@@ -717,7 +797,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
   if (nsteps > 0) for (int pass = 0;; ++pass) {
     if (pass > 0) {
-      if constexpr (SPARSE) {
+      if constexpr (SPARSE && FP8) {
+        f8_load_ids();
+      } else if constexpr (SPARSE) {
 #pragma unroll
         for (int it = 0; it < NB; ++it) sidx_pro[it] = idx_row[idx_of(it)];
       } else {
@@ -732,7 +814,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
     }
-    if constexpr (SPARSE) {
+    if constexpr (SPARSE && !FP8) {
 #pragma unroll
       for (int it = 0; it < NB - 1; ++it) {
         sidx = sidx_pro[it];
@@ -741,7 +823,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       sidx = sidx_pro[NB - 1];
     } else if constexpr (FP8) {
       // tiles 0 and 1: codes, scales and rope values
+#pragma unroll
       for (int it = 0; it < 2; ++it) {
+        if constexpr (SPARSE) {
+          f8c = f8_id_at(it, f8_rc);
+          f8s = f8_id_at(it, f8_rs);
+          f8r = f8_id_at(it, f8_rr);
+        }
         issue_prep(it);
         f8_rope_prep(it);
         f8_issue_part(std::integral_constant<int, 0>{});
@@ -769,6 +857,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         f8_convert(0);
         f8_convert(1);
         wait_lgkm0();
+        if constexpr (SPARSE) {
+          f8c = f8_id_at(2, f8_rc);
+          f8s = f8_id_at(2, f8_rs);
+        }
         issue_prep(2);
         f8_issue_codes();
       } else {
@@ -841,22 +933,26 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           if constexpr (f8_part_at(s) >= 0) f8_issue_part(std::integral_constant<int, f8_part_at(s)>{});
           // the previous step's loads (codes of tile i+2) have landed once at most
           // this step's six are in flight
-          if constexpr (s == kF8Wait) wait_vm<6>();
+          if constexpr (s == kF8Wait) {
+            wait_vm<SPARSE ? 7 : 6>();
+            f8_bases(i + 2);   // (here, not at the step start: short live ranges)
+          }
           constexpr int cv = f8_cvt_at(s);
           if constexpr (cv >= 0) {
             constexpr int n = cv >> 2, ph = cv & 3;
-            if constexpr (ph == 0) f8_read(i + 2, std::integral_constant<int, n>{});
-            else f8_write(i + 2, std::integral_constant<int, n>{}, std::integral_constant<int, ph - 1>{});
+            if constexpr (ph == 0) f8_read(std::integral_constant<int, n>{});
+            else f8_write(std::integral_constant<int, n>{}, std::integral_constant<int, ph - 1>{});
           }
         } else if constexpr (dma_part_at(s) >= 0) {
           issue_part(std::integral_constant<int, dma_part_at(s)>{});
         }
-        if constexpr (SPARSE && s == kSpIds) {
+        if constexpr (SPARSE && !FP8 && s == kSpIds) {
           // the ids of step i + NB have landed once at most the nine tile loads
           // issued after them are in flight
           wait_vm<9>();
           sidx = *(const __attribute__((address_space(3))) int*)(uintptr_t)(ids_lds(i) + 4 * (16 * hw + rsw));
         }
+
         // softmax of step i+1 (past the last step every score is masked)
         if constexpr (s == kSmLoad) {
           sm_load(Sn);
@@ -886,6 +982,14 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       // this wave's probability writes are done; the last two V operand reads
       // (two LDS reads each) may stay in flight
       wait_lgkm<4>();
+      if constexpr (SPARSE && FP8) {
+        // row ids of this step's loads (codes and scales of step i + 3, rope of
+        // step i + 2), in LDS since the wait above (their load preceded the
+        // rope values of step i + 1); read under the barrier
+        f8c = f8_id_at(i + 3, f8_rc);
+        f8s = f8_id_at(i + 3, f8_rs);
+        f8r = f8_id_at(i + 2, f8_rr);
+      }
       barrier();
       if (i + 2 == nsteps && j1 - (j0 + kStepTok * (i + 1)) < kStepTok) {
         // the last step is partial: clear its rows past the end before any
@@ -1130,8 +1234,15 @@ hipError_t launch_decode(const DecodeParams& prm, int max_units, bool split, boo
                          hipStream_t st, bool sparse, bool fp8) {
   constexpr int NB = 4;
   const int grid = ((max_units + 7) / 8) * 8;  // whole XCD rounds; extra workgroups exit
+  if (fp8 && sparse) {
+    if (split) {
+      if (out_f32) return launch_decode_t<3, true, true, true, true>(prm, grid, st);
+      return launch_decode_t<3, true, false, true, true>(prm, grid, st);
+    }
+    if (out_f32) return launch_decode_t<3, false, true, true, true>(prm, grid, st);
+    return launch_decode_t<3, false, false, true, true>(prm, grid, st);
+  }
   if (fp8) {
-    if (sparse) return hipErrorInvalidValue;
     if (split) {
       if (out_f32) return launch_decode_t<3, true, true, false, true>(prm, grid, st);
       return launch_decode_t<3, true, false, false, true>(prm, grid, st);

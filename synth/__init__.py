@@ -445,11 +445,19 @@ def make_fp8_case(wl: Workload, poison: bool = True) -> Fp8Case:
     With ``poison``, every row no sequence may read holds NaN codes, NaN
     scales and the bf16 NaN rope values of ``make_case``."""
     case = make_case(wl, poison=poison)
-    rng = np.random.Generator(np.random.PCG64(wl.seed + 0xF8))
-    nb, P = case.kv_cache.shape[0], wl.page_size
-    r = wl.r
-    if r != 512 or wl.d_rope != 64:
+    if wl.r != 512 or wl.d_rope != 64:
         raise ValueError("the FP8 row holds 512 latent and 64 rope values")
+    return Fp8Case(case, _fp8_rows(wl.seed, case.kv_cache, poison))
+
+
+def _fp8_rows(seed: int, bf16_rows: np.ndarray, poison: bool) -> np.ndarray:
+    """FP8 rows [num_blocks, P, 656] for a pool whose bf16 rows are ``bf16_rows``:
+    codes and scales drawn from ``Generator(PCG64(seed + 0xF8))`` (see
+    ``make_fp8_case``), rope values copied from the bf16 rows; with ``poison``,
+    rows whose bf16 latent is NaN get NaN codes and NaN scales."""
+    rng = np.random.Generator(np.random.PCG64(seed + 0xF8))
+    nb, P, _ = bf16_rows.shape
+    r = 512
     mag = np.clip(np.rint(rng.normal(108.0, 10.0, size=(nb, P, r))), 0, 126).astype(np.uint8)
     sign = rng.integers(0, 2, size=(nb, P, r), dtype=np.uint8) << np.uint8(7)
     codes = mag | sign
@@ -457,9 +465,26 @@ def make_fp8_case(wl: Workload, poison: bool = True) -> Fp8Case:
     rows = np.empty((nb, P, FP8_ROW_BYTES), dtype=np.uint8)
     rows[:, :, :512] = codes
     rows[:, :, 512:528] = scales.astype("<f4").view(np.uint8).reshape(nb, P, 16)
-    rows[:, :, 528:] = np.ascontiguousarray(case.kv_cache[:, :, r:]).astype("<u2").view(np.uint8).reshape(nb, P, 128)
+    rows[:, :, 528:] = np.ascontiguousarray(bf16_rows[:, :, r:]).astype("<u2").view(np.uint8).reshape(nb, P, 128)
     if poison:
-        dead = np.isnan(bf16_bits_to_f32(case.kv_cache[:, :, r]))   # rows make_case poisoned
+        dead = np.isnan(bf16_bits_to_f32(bf16_rows[:, :, r]))   # rows the bf16 generator poisoned
         rows[dead, :512] = FP8_NAN_CODE
         rows[dead, 512:528] = np.full(4, F32_NAN_BITS, dtype="<u4").view(np.uint8)
-    return Fp8Case(case, rows)
+    return rows
+
+
+@dataclasses.dataclass
+class SparseFp8Case:
+    """A sparse decode workload over FP8 rows: ``sparse`` supplies queries,
+    index rows and valid prefixes (its bf16 ``kv_cache`` is not read by the
+    FP8 path); ``kv_fp8`` holds the pool's rows."""
+    sparse: SparseCase
+    kv_fp8: np.ndarray   # [num_blocks, P, 656] uint8
+
+
+def make_sparse_fp8(wl: Workload, topk: int, **kw) -> SparseFp8Case:
+    """``make_sparse(wl, topk, **kw)``, then the pool's rows as FP8 rows drawn as
+    in ``make_fp8_case`` (codes, scales; rope values from the bf16 rows; rows no
+    index selects are NaN when ``poison``)."""
+    sc = make_sparse(wl, topk, **kw)
+    return SparseFp8Case(sc, _fp8_rows(wl.seed, sc.kv_cache, kw.get("poison", True)))

@@ -248,6 +248,11 @@ void test_merge_append_sparse() {
   EXPECT_EQ(mla_decode_sparse(Q, Q, Q, 512, 64, (int32_t*)D, 2048, nullptr, 64, 1, 128, 512, 64, 0.07f, 1, nullptr,
                               MLA_BF16, nullptr, nullptr, D, MLA_BF16, nullptr, nullptr), MLA_OK);
   EXPECT(rec.decode == 1 && !rec.split && rec.dp.n_units == 64);
+  rec = Rec{};
+  EXPECT_EQ(mla_decode_sparse_fp8(Q, Q, (const uint8_t*)D, 512, 64, (int32_t*)D, 2048, nullptr, 64, 1, 128, 512, 64,
+                                  0.07f, 0, D, MLA_BF16, (float*)D, (int32_t*)D, D, MLA_BF16, nullptr, nullptr),
+            MLA_OK);
+  EXPECT(rec.decode == 1 && rec.sparse && rec.fp8 && rec.split && rec.merge == 1);
   EXPECT_EQ(mla_decode_sparse(Q, Q, Q, 1 << 27, 64, (int32_t*)D, 2048, nullptr, 64, 1, 128, 512, 64, 0.07f, 1,
                               nullptr, MLA_BF16, nullptr, nullptr, D, MLA_BF16, nullptr, nullptr),
             MLA_ERR_UNSUPPORTED);   // more than 2^32 - 1 rows
