@@ -62,7 +62,7 @@ def chain_algorithmic(case, decode_bytes):
     return decode_bytes + absorb + unabsorb
 
 
-def sparse_algorithmic(sc):
+def sparse_algorithmic(sc, row_bytes=ROW_BYTES):
     """Algorithmic bytes and FLOPs of one sparse decode launch, counted as for the
     dense kernel: every valid selected row once with its index entry, the
     query, the bf16 latent output and the lse.  Split partials are overhead of
@@ -73,24 +73,30 @@ def sparse_algorithmic(sc):
     keys = int(np.sum(n)) * T if sc.topk_length is not None else B * T * sc.topk
     q_bytes = B * T * H * (512 + 64) * 2
     out_bytes = B * T * H * (512 * 2 + 4)
-    nbytes = keys * (ROW_BYTES + 4) + q_bytes + out_bytes
+    nbytes = keys * (row_bytes + 4) + q_bytes + out_bytes
     flops = 2 * H * keys * (576 + 512)
     return nbytes, flops
 
 
-def bench_sparse(name, K, W, R, dev):
+def bench_sparse(name, K, W, R, dev, fp8=False):
     """Time the sparse (top-k) decode kernel on its workload: HIP events around
-    each launch on its stream, cache replicas rotating."""
+    each launch on its stream, cache replicas rotating.  ``fp8``: the same
+    selections over a pool of 656-byte FP8 rows (fields prefixed sparse_fp8_)."""
     import numpy as np
     import torch
     import mla_latent_kv_amd as mk
     import synth
-    sc = synth.make_sparse(synth.SPARSE_WORKLOADS[name], synth.SPARSE_TOPK[name], poison=False)
+    if fp8:
+        f = synth.make_sparse_fp8(synth.SPARSE_WORKLOADS[name], synth.SPARSE_TOPK[name], poison=False)
+        sc = f.sparse
+    else:
+        sc = synth.make_sparse(synth.SPARSE_WORKLOADS[name], synth.SPARSE_TOPK[name], poison=False)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    kv0 = bf16(sc.kv_cache)
+    kv0 = torch.from_numpy(f.kv_fp8).to(dev) if fp8 else bf16(sc.kv_cache)
+    decode = mk.mla_decode_sparse_fp8 if fp8 else mk.mla_decode_sparse
     kv = [kv0] + [kv0.clone() for _ in range(R - 1)]
     q_lat, q_pe = bf16(sc.q_lat), bf16(sc.q_pe)
     idx = torch.from_numpy(sc.indices).to(dev)
@@ -106,7 +112,7 @@ def bench_sparse(name, K, W, R, dev):
     def run(r, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        mk.mla_decode_sparse(q_lat, q_pe, kv[r], idx, tl, scale, buffers=buf, merge=False)
+        decode(q_lat, q_pe, kv[r], idx, tl, scale, buffers=buf, merge=False)
         if ev is not None:
             ev[1].record(stream)
         if S > 1:
@@ -124,11 +130,12 @@ def bench_sparse(name, K, W, R, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
-    nbytes, flops = sparse_algorithmic(sc)
+    nbytes, flops = sparse_algorithmic(sc, 656 if fp8 else ROW_BYTES)
     del kv, kv0
     torch.cuda.empty_cache()
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", "decode_sparse_hbm_traffic.json")
+    tpath = os.path.join(ROOT, "profiles", "decode_sparse_fp8_hbm_traffic.json" if fp8 else
+                         "decode_sparse_hbm_traffic.json")
     if os.path.exists(tpath):
         try:
             from mla_latent_kv_amd import _build
@@ -138,16 +145,18 @@ def bench_sparse(name, K, W, R, dev):
                 traffic = rec["bytes_per_launch"]
         except Exception:
             traffic = None
+    pre = "sparse_fp8_" if fp8 else "sparse_"
     return {
-        "sparse_workload": name, "sparse_topk": sc.topk, "sparse_context": int(sc.seqlens.max()),
-        "sparse_splits": S,
-        "sparse_decode_us": us,
-        "sparse_step_us": (t1 - t0) * 1e6 / K,
-        "sparse_alg_bytes": nbytes,
-        "sparse_GBps": nbytes / (us * 1e-6) / 1e9,
-        "sparse_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-        "sparse_tflops": flops / (us * 1e-6) / 1e12,
-        "sparse_traffic": traffic,
+        pre + "workload": name, pre + "topk": sc.topk, pre + "context": int(sc.seqlens.max()),
+        pre + "splits": S,
+        pre + "decode_us": us,
+        pre + "step_us": (t1 - t0) * 1e6 / K,
+        pre + "alg_bytes": nbytes,
+        pre + "GBps": nbytes / (us * 1e-6) / 1e9,
+        pre + "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        pre + "tflops": flops / (us * 1e-6) / 1e12,
+        pre + "mfma_frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        pre + "traffic": traffic,
     }
 
 
@@ -516,6 +525,71 @@ def power_roof(seconds, dev):
     return out
 
 
+# decode kernel instantiation -> (workload, splits, partials, record file) in a
+# run of `bench.py --no-cpu --no-workloads --roof-seconds 0 --copy-calibration`
+TRAFFIC_RECORDS = {
+    "void mla::decode_kernel<4, true, false, false, false>(mla::DecodeParams)":
+        (HEADLINE, 4, "bf16", "decode_hbm_traffic.json"),
+    "void mla::decode_kernel<3, true, false, false, true>(mla::DecodeParams)":
+        ("v3_fp8_b64_l4096", 4, "bf16", "decode_fp8_hbm_traffic.json"),
+    "void mla::decode_kernel<4, true, false, true, false>(mla::DecodeParams)":
+        ("v3_sparse_b64_topk2048", 4, "bf16", "decode_sparse_hbm_traffic.json"),
+    "void mla::decode_kernel<3, true, false, true, true>(mla::DecodeParams)":
+        ("v3_sparse_b64_topk2048", 4, "bf16", "decode_sparse_fp8_hbm_traffic.json"),
+}
+
+
+def traffic_record(fetch_csv, write_csv):
+    """HBM bytes per launch of each decode kernel from two rocprofv3 counter
+    passes (FETCH_SIZE, then WRITE_SIZE; per-dispatch CSVs): the median over
+    the kernel's dispatches, scaled by what the same counter reads for the
+    benchmark's 1 GiB device-to-device copies (2^30 bytes read and written).  Writes
+    one record per kernel under profiles/ (with the decode sources' hash, so
+    the benchmark reports it only while the kernel is unchanged)."""
+    import csv
+    import statistics
+    from mla_latent_kv_amd import _build
+
+    def per_dispatch(path, counter):
+        sums = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+        return sums
+
+    fetch_d = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write_d = per_dispatch(write_csv, "WRITE_SIZE")
+    # the 1 GiB device-to-device copies (the context measurement and the
+    # calibration copy) are the copy dispatches that wrote exactly 2^20 KiB; the
+    # two passes launch the same dispatches in the same order
+    cal = [key for key, v in write_d.items() if "copyBuffer" in key[0] and v == float(1 << 20)]
+    if not cal or any(key not in fetch_d for key in cal):
+        raise SystemExit("no 1 GiB calibration copy in both counter passes (run bench.py with --copy-calibration)")
+    fetch_factor = (1 << 30) / (statistics.median(fetch_d[k] for k in cal) * 1024)   # bytes per counted KiB
+    write_factor = (1 << 30) / (statistics.median(write_d[k] for k in cal) * 1024)
+    fetch, write = {}, {}
+    for (k, _), v in fetch_d.items():
+        fetch.setdefault(k, []).append(v)
+    for (k, _), v in write_d.items():
+        write.setdefault(k, []).append(v)
+    out = []
+    for kname, (workload, splits, partials, fname) in TRAFFIC_RECORDS.items():
+        if kname not in fetch or kname not in write:
+            continue
+        rd = statistics.median(fetch[kname]) * 1024 * fetch_factor
+        wr = statistics.median(write[kname]) * 1024 * write_factor
+        rec = {"workload": workload, "kernel": kname, "source_sha256": _build.kernel_source_hash(),
+               "bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+               "fetch_factor": fetch_factor, "write_factor": write_factor, "splits": splits, "partials": partials,
+               "dispatches": len(fetch[kname])}
+        with open(os.path.join(ROOT, "profiles", fname), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        out.append(rec)
+    return out
+
+
 def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys).
@@ -740,11 +814,18 @@ def main():
     ap.add_argument("--roof-seconds", type=float, default=1.0,
                     help="seconds per practical-roof probe and half the seconds of the decode clock sample "
                          "reported under detail (0 skips them)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="instead of the benchmark line: write the decode kernels' HBM traffic records under "
+                         "profiles/ from two rocprofv3 counter_collection CSVs (FETCH_SIZE pass, WRITE_SIZE pass)")
     ap.add_argument("--power-roof", type=float, default=0.0,
                     help="instead of the benchmark line: run the practical-roof probes for this many seconds each "
                          "(one JSON line per probe)")
     args = ap.parse_args()
 
+    if args.traffic_record:
+        for rec in traffic_record(*args.traffic_record):
+            print(json.dumps(rec), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path does not shard across GPUs "
               "(one process, one device); run it with --gpus 1.", file=sys.stderr)
@@ -905,6 +986,8 @@ def main():
         result["detail"]["power_roof"] = power_roof(args.roof_seconds, dev)
     if not args.no_sparse:
         result["detail"].update(bench_sparse("v3_sparse_b64_topk2048", K, args.warmup, R, dev))
+        if not args.no_fp8:
+            result["detail"].update(bench_sparse("v3_sparse_b64_topk2048", K, args.warmup, R, dev, fp8=True))
     if not args.no_fp8:
         result["detail"].update(bench_fp8("v3_fp8_b64_l4096", 4, K, args.warmup, R, dev))
     if not args.no_cpu:

@@ -77,14 +77,19 @@ def build(verbose: bool = False) -> str:
 
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel and ABI sources with comments and whitespace
+# sources the decode kernel is built from (a stored counter record of the
+# decode kernel stays valid while these are unchanged)
+DECODE_SOURCES = ("decode_latent.hip", "common.hpp", "launch.hpp")
+
+
+def kernel_source_hash(names=DECODE_SOURCES) -> str:
+    """sha256 over the named kernel sources with comments and whitespace
     removed (identifies which code a stored counter measurement belongs to;
     editing a comment does not change it)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names):
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
