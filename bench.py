@@ -811,7 +811,7 @@ def main():
     ap.add_argument("--clock-kernel", choices=["bf16", "fp8"], default="bf16")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the driver-timed lines of the other configurations (detail.workloads)")
-    ap.add_argument("--roof-seconds", type=float, default=1.0,
+    ap.add_argument("--roof-seconds", type=float, default=2.5,
                     help="seconds per practical-roof probe and half the seconds of the decode clock sample "
                          "reported under detail (0 skips them)")
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
