@@ -609,6 +609,39 @@ def traffic_record(fetch_csv, write_csv):
     return out
 
 
+def trace_segments(trace_csv, kernel=None):
+    """Per-kernel durations from a rocprofv3 kernel-trace CSV: for each decode
+    kernel, the mean over all its dispatches (what --stats reports) and the mean
+    over its longest run of consecutive dispatches with no other kernel between
+    them (the benchmark's back-to-back segment, which the roofline figure times),
+    both as kernel durations and as the segment's span (first start to last end)
+    per dispatch."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    out = []
+    for kname in sorted(set(names)):
+        if "decode_kernel" not in kname or (kernel and kernel not in kname):
+            continue
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in rows
+                if r["Kernel_Name"] == kname]
+        best, run = (0, 0), None
+        for i, n in enumerate(names + [None]):
+            if n == kname:
+                run = i if run is None else run
+            elif run is not None:
+                if i - run > best[1] - best[0]:
+                    best = (run, i)
+                run = None
+        seg = rows[best[0]:best[1]]
+        seg_d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3 for r in seg]
+        span = (int(seg[-1]["End_Timestamp"]) - int(seg[0]["Start_Timestamp"])) * 1e-3 / len(seg)
+        out.append({"kernel": kname, "dispatches": len(durs), "mean_us": sum(durs) / len(durs),
+                    "b2b_dispatches": len(seg), "b2b_mean_us": sum(seg_d) / len(seg_d),
+                    "b2b_span_us_per_dispatch": span})
+    return out
+
+
 def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
     """Time the CPU oracle (fp64 Normal path) on a seeded sample of (b, h) pairs
     and scale linearly to the whole batch (its cost is linear in pairs x keys).
@@ -856,6 +889,9 @@ def main():
     ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="instead of the benchmark line: write the decode kernels' HBM traffic records under "
                          "profiles/ from two rocprofv3 counter_collection CSVs (FETCH_SIZE pass, WRITE_SIZE pass)")
+    ap.add_argument("--trace-segments", metavar="KERNEL_TRACE_CSV",
+                    help="instead of the benchmark line: each decode kernel's mean duration over all dispatches and "
+                         "over its back-to-back segment, from a rocprofv3 kernel-trace CSV")
     ap.add_argument("--power-roof", type=float, default=0.0,
                     help="instead of the benchmark line: run the practical-roof probes for this many seconds each "
                          "(one JSON line per probe)")
@@ -863,6 +899,10 @@ def main():
 
     if args.traffic_record:
         for rec in traffic_record(*args.traffic_record):
+            print(json.dumps(rec), flush=True)
+        return
+    if args.trace_segments:
+        for rec in trace_segments(args.trace_segments):
             print(json.dumps(rec), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
