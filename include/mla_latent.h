@@ -20,6 +20,9 @@
  *   mla_unabsorb_out   out = W_UV latent                ("MLA in full detail", Step 4:
  *                                                       fold W_UV into the output)
  *
+ * mla_merge_unabsorb takes the last two in one kernel (split partials in, out
+ * and lse out; the merged latent never goes to memory).
+ *
  * and, for multi-step decoding, mla_append_cache (the new tokens' cache rows
  * written at their paged positions before the decode that reads them); for
  * sparse (top-k) attention, mla_decode_sparse (bf16 rows) and
@@ -279,6 +282,29 @@ int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* pa
  * (einsum bhqc,hvc->bhqv; W_UV [H,d_V,d_c]). */
 int mla_unabsorb_out(const void* latent, mla_dtype latent_dtype, const uint16_t* w_uv, float* out,
                      int B, int T, int H, int r, int d_V, void* stream);
+
+/* Merge of split partials and un-absorb in one launch: the merge of
+ * mla_merge_splits with a bf16 out_latent, followed by mla_unabsorb_out of that
+ * latent.  The merged rows are rounded to bf16 in on-chip memory and multiplied
+ * by W_UV there; only out and lse are written.
+ *   part_out [*,T,H,r] f32 or bf16 (part_dtype), part_lse [*,T,H] f32,
+ *   split_indptr [B+1] int32 (rows of each (b) as written by mla_decode_latent
+ *   or mla_decode_sparse with merge left to the caller), w_uv [H,d_V,r] bf16
+ *   out [B,T,H,d_V] f32, lse [B,T,H] f32 (nullable; the merged lse)
+ * Errors (nothing is launched): MLA_ERR_SHAPE for B < 0, T < 1, H < 1 or
+ * B*T > 2^24; MLA_ERR_UNSUPPORTED for r != 512, d_V != 128, T > 1024, H > 128
+ * or another part_dtype; MLA_ERR_NULL / MLA_ERR_ALIGN for pointers.  B == 0
+ * is a no-op.  Rows with no split (split_indptr[b] == split_indptr[b+1]) give
+ * out = 0 and lse = -inf.  Results equal the two separate calls' (lse bit for
+ * bit, out up to the order of the fp32 sums).  Faster than those calls when
+ * every row has at most four splits and the partials are bf16 (a 32-row
+ * block's loads all go out before any arithmetic); with more splits a row is
+ * merged by one wave at a time and the separate calls are faster.
+ * Sources: M5.8 0x0C (exact merge of split states) and "MLA in full detail",
+ * Step 4 (W_UV folded into the output). */
+int mla_merge_unabsorb(const void* part_out, mla_dtype part_dtype, const float* part_lse,
+                       const int32_t* split_indptr, const uint16_t* w_uv, int B, int T, int H, int r, int d_V,
+                       float* out, float* lse, void* stream);
 
 /* Cache append: writes the T new rows [c (r) || k_pe (d_R)] of every sequence
  * into the paged cache, new row t of sequence b at logical position

@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
 * ``mla_decode_latent_fp8``  the same over 656-byte FP8 rows    (M5.8 0x0B)
 * ``mla_merge_splits``  log-sum-exp merge of split partials   (M5.8 0x0C)
 * ``mla_unabsorb_out``  out = W_UV latent                    ("MLA in full detail", Step 4)
+* ``mla_merge_unabsorb``  the merge and the un-absorb in one kernel (no latent round trip)
 * ``mla_append_cache``  new tokens' rows into the paged cache (M5.8 0x05)
 * ``mla_decode_sparse``  top-k latent attention over physical row ids (M5.8 0x0B)
 * ``mla_decode_workspace_size``, ``mla_validate_inputs``, ``mla_status_string``
@@ -69,6 +70,7 @@ def load_library():
     L.mla_decode_latent_noalloc.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, I, F, I, P, I, P, P]
     L.mla_merge_splits.argtypes = [P, I, P, P, I, I, I, I, P, I, P, P]
     L.mla_unabsorb_out.argtypes = [P, I, P, P, I, I, I, I, I, P]
+    L.mla_merge_unabsorb.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, P]
     L.mla_append_cache.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, P]
     L.mla_sparse_split_count.argtypes = [I, I, I, I, I, P]
     L.mla_decode_sparse.argtypes = [P, P, P, I, I, P, I, P, I, I, I, I, I, F, I, P, I, P, P, P, I, P, P]
@@ -77,7 +79,7 @@ def load_library():
     for name in ("mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent",
                  "mla_merge_splits", "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count",
                  "mla_decode_sparse", "mla_validate_inputs", "mla_decode_latent_fp8",
-                 "mla_decode_latent_noalloc", "mla_decode_sparse_fp8"):
+                 "mla_decode_latent_noalloc", "mla_decode_sparse_fp8", "mla_merge_unabsorb"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -378,6 +380,34 @@ def mla_unabsorb_out(latent, w_uv, out=None, stream=None):
     return out
 
 
+def mla_merge_unabsorb(part_out, part_lse, split_indptr, w_uv, B, out=None, lse=None, stream=None):
+    """Merge of split partials and un-absorb in one kernel:
+    part_out [*,T,H,512] f32/bf16, part_lse [*,T,H] f32, split_indptr [B+1] int32,
+    w_uv [H,128,512] bf16 -> (out [B,T,H,128] f32, lse [B,T,H] f32)."""
+    torch = _torch()
+    _need(part_out, (torch.bfloat16, torch.float32), "mla_merge_unabsorb part_out")
+    _need(part_lse, (torch.float32,), "mla_merge_unabsorb part_lse")
+    _need(split_indptr, (torch.int32,), "mla_merge_unabsorb split_indptr")
+    _need(w_uv, (torch.bfloat16,), "mla_merge_unabsorb w_uv")
+    _need(out, (torch.float32,), "mla_merge_unabsorb out")
+    _need(lse, (torch.float32,), "mla_merge_unabsorb lse")
+    _, T, H, r = part_out.shape
+    dv = w_uv.shape[1]
+    _shape(part_lse, (part_out.shape[0], T, H), "mla_merge_unabsorb part_lse")
+    _shape(split_indptr, (B + 1,), "mla_merge_unabsorb split_indptr")
+    _shape(w_uv, (H, dv, r), "mla_merge_unabsorb w_uv")
+    _shape(out, (B, T, H, dv), "mla_merge_unabsorb out")
+    _shape(lse, (B, T, H), "mla_merge_unabsorb lse")
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=part_out.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=part_out.device)
+    _check(load_library().mla_merge_unabsorb(_ptr(part_out), _dtype_code(part_out.dtype), _ptr(part_lse),
+                                             _ptr(split_indptr), _ptr(w_uv), B, T, H, r, dv, _ptr(out),
+                                             _ptr(lse), _stream(stream)), "mla_merge_unabsorb")
+    return out, lse
+
+
 def mla_append_cache(c_new, kpe_new, kv_cache, block_table, seqlens, stream=None):
     """Write the T new rows of every sequence at positions seqlens[b]-T+t of the
     paged cache (in place).  c_new [B,T,512] bf16, kpe_new [B,T,64] bf16."""
@@ -571,7 +601,8 @@ __all__ = [
     "MLA_BF16", "MLA_F32", "MLAError", "load_library", "load_normal_library", "status_string", "mla_status_string",
     "mla_absorb_q", "mla_decode_workspace_size", "mla_decode_latent", "mla_decode_latent_fp8",
     "mla_decode_latent_noalloc", "mla_merge_splits",
-    "mla_unabsorb_out", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse", "mla_decode_sparse_fp8",
+    "mla_unabsorb_out", "mla_merge_unabsorb", "mla_append_cache", "mla_sparse_split_count", "mla_decode_sparse",
+    "mla_decode_sparse_fp8",
     "SparseBuffers",
     "mla_normal_workspace_size", "mla_decode_normal", "mla_validate_inputs", "DecodeBuffers", "softmax_scale",
     "absorbed_decode",

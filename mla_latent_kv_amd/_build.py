@@ -22,7 +22,8 @@ NORMAL_LIB = os.path.join(HERE, "libmla_normal.so")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 # library -> (sources, extra link flags)
 LIBRARIES = {
-    LIB: (["api.cpp", "decode_latent.hip", "merge_splits.hip", "bmm.hip", "append.hip", "noalloc.hip"], []),
+    LIB: (["api.cpp", "decode_latent.hip", "merge_splits.hip", "merge_unabsorb.hip", "bmm.hip", "append.hip",
+           "noalloc.hip"], []),
     NORMAL_LIB: (["normal_api.cpp", "normal.hip"],
                  ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]),
     PROBE_LIB: (["roof_probe.hip"], []),

@@ -403,6 +403,35 @@ int mla_merge_splits(const void* part_out, mla_dtype part_dtype, const float* pa
       mla::launch_merge(mp, part_dtype == MLA_F32, out_dtype == MLA_F32, (hipStream_t)stream));
 }
 
+// Workgroups per head of the merge + un-absorb kernel: enough row blocks per
+// head to give each of the 256 CUs one workgroup, never more than there are
+// blocks (a workgroup holds one head's W_UV in LDS for all the blocks it takes).
+static int merge_unabsorb_groups(int M, int H) {
+  const int blocks = (M + mla::kMergeUnabsorbRows - 1) / mla::kMergeUnabsorbRows;
+  const int want = (256 + H - 1) / H;
+  return blocks < want ? blocks : want;
+}
+
+int mla_merge_unabsorb(const void* part_out, mla_dtype part_dtype, const float* part_lse,
+                       const int32_t* split_indptr, const uint16_t* w_uv, int B, int T, int H, int r, int d_V,
+                       float* out, float* lse, void* stream) {
+  if (B < 0) return MLA_ERR_SHAPE;
+  int st = check_heads(T, H);
+  if (st) return st;
+  if (r != kR || d_V != kDV) return MLA_ERR_UNSUPPORTED;
+  if (part_dtype != MLA_BF16 && part_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (B == 0) return MLA_OK;
+  if ((st = check_ptr16(part_out)) || (st = check_ptr4(part_lse)) || (st = check_ptr4(split_indptr)) ||
+      (st = check_ptr16(w_uv)) || (st = check_ptr16(out)))
+    return st;
+  if (lse && !aligned4(lse)) return MLA_ERR_ALIGN;
+  if ((long long)B * T > (1LL << 24)) return MLA_ERR_SHAPE;
+  const int M = B * T;
+  mla::MergeUnabsorbParams p{part_out, part_lse, split_indptr, w_uv, out, lse, M, T, H,
+                             merge_unabsorb_groups(M, H)};
+  return launch_status(mla::launch_merge_unabsorb(p, part_dtype == MLA_F32, (hipStream_t)stream));
+}
+
 int mla_validate_inputs(const int32_t* block_table, int max_blocks_per_seq,
                         const int32_t* seqlens, int B, int T, int max_seqlen, int page_size,
                         int num_blocks, void* stream) {

@@ -64,6 +64,21 @@ struct UnabsorbParams {
   int M, H;
 };
 
+// Query rows per block of the merge + un-absorb kernel (one workgroup takes
+// blocks j, j + groups, ... of one head).
+constexpr int kMergeUnabsorbRows = 32;
+
+struct MergeUnabsorbParams {
+  const void* part_out;        // [*,T,H,512] f32 or bf16 (split rows of split_indptr)
+  const float* part_lse;       // [*,T,H]
+  const int32_t* split_indptr; // [B+1]
+  const uint16_t* w_uv;        // [H,128,512]
+  float* out;                  // [B,T,H,128]
+  float* lse;                  // [B,T,H], nullable
+  int M, T, H;                 // M = B*T query rows
+  int groups;                  // workgroups per head, 1 .. ceil(M / kMergeUnabsorbRows)
+};
+
 struct AppendParams {
   const uint16_t* c_new;       // [B,T,512] bf16
   const uint16_t* kpe_new;     // [B,T,64] bf16
@@ -99,6 +114,7 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, bool part_f32, bool out_f32, hipStream_t st);
 hipError_t launch_absorb(const AbsorbParams& p, hipStream_t st);
 hipError_t launch_unabsorb(const UnabsorbParams& p, bool latent_f32, hipStream_t st);
+hipError_t launch_merge_unabsorb(const MergeUnabsorbParams& p, bool part_f32, hipStream_t st);
 hipError_t launch_append(const AppendParams& p, hipStream_t st);
 hipError_t launch_gather(const NormalParams& p, hipStream_t st);
 hipError_t launch_mha(const NormalParams& p, hipStream_t st);

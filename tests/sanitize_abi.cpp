@@ -25,12 +25,15 @@
 
 namespace {
 struct Rec {
-  int decode = 0, plan = 0, merge = 0, absorb = 0, unabsorb = 0, append = 0, gather = 0, mha = 0, gemm = 0;
+  int decode = 0, plan = 0, merge = 0, absorb = 0, unabsorb = 0, append = 0, gather = 0, mha = 0, gemm = 0,
+      merge_unabsorb = 0;
   mla::DecodeParams dp{};
   int max_units = 0;
   bool split = false, out_f32 = false, sparse = false, fp8 = false;
   mla::PlanParams pp{};
   mla::MergeParams mp{};
+  mla::MergeUnabsorbParams mup{};
+  bool mu_f32 = false;
   int absorb_M = 0, unabsorb_M = 0;
 } rec;
 int failures = 0;
@@ -76,6 +79,12 @@ hipError_t launch_absorb(const AbsorbParams& p, hipStream_t) {
 hipError_t launch_unabsorb(const UnabsorbParams& p, bool, hipStream_t) {
   ++rec.unabsorb;
   rec.unabsorb_M = p.M;
+  return hipSuccess;
+}
+hipError_t launch_merge_unabsorb(const MergeUnabsorbParams& p, bool part_f32, hipStream_t) {
+  ++rec.merge_unabsorb;
+  rec.mup = p;
+  rec.mu_f32 = part_f32;
   return hipSuccess;
 }
 hipError_t launch_append(const AppendParams&, hipStream_t) {
@@ -228,6 +237,40 @@ void test_merge_append_sparse() {
             MLA_ERR_UNSUPPORTED);
   EXPECT_EQ(mla_merge_splits(D, MLA_BF16, (float*)Dmis, (int32_t*)D, 64, 1, 128, 512, D, MLA_BF16, nullptr,
                              nullptr), MLA_ERR_ALIGN);
+  // merge + un-absorb: the grid (heads x groups) and its validation
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 64, 1, 128, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_OK);
+  EXPECT(rec.mup.M == 64 && rec.mup.T == 1 && rec.mup.H == 128 && rec.mup.groups == 2 && !rec.mu_f32);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_F32, (float*)D, (int32_t*)D, Q, 32, 4, 32, 512, 128, (float*)D, (float*)D,
+                               nullptr), MLA_OK);
+  EXPECT(rec.mup.M == 128 && rec.mup.groups == 4 && rec.mu_f32);   // 4 blocks, up to 8 wanted
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 1, 1, 1, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_OK);
+  EXPECT(rec.mup.groups == 1);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 1, 1024, 1, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_OK);
+  EXPECT(rec.mup.groups == 32);                                   // 32 blocks of one head
+  const int mu_calls = rec.merge_unabsorb;
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 64, 1, 128, 256, 128, (float*)D, nullptr,
+                               nullptr), MLA_ERR_UNSUPPORTED);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 64, 1, 129, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_ERR_UNSUPPORTED);
+  EXPECT_EQ(mla_merge_unabsorb(D, (mla_dtype)7, (float*)D, (int32_t*)D, Q, 64, 1, 128, 512, 128, (float*)D,
+                               nullptr, nullptr), MLA_ERR_UNSUPPORTED);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)Dmis, (int32_t*)D, Q, 64, 1, 128, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_ERR_ALIGN);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 64, 1, 128, 512, 128, (float*)D,
+                               (float*)Dmis, nullptr), MLA_ERR_ALIGN);
+  EXPECT_EQ(mla_merge_unabsorb(nullptr, MLA_BF16, (float*)D, (int32_t*)D, Q, 64, 1, 128, 512, 128, (float*)D,
+                               nullptr, nullptr), MLA_ERR_NULL);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, -1, 1, 128, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_ERR_SHAPE);
+  EXPECT_EQ(mla_merge_unabsorb(D, MLA_BF16, (float*)D, (int32_t*)D, Q, 1 << 24, 2, 1, 512, 128, (float*)D, nullptr,
+                               nullptr), MLA_ERR_SHAPE);
+  EXPECT_EQ(rec.merge_unabsorb, mu_calls);                        // nothing launched on an error
+  EXPECT_EQ(mla_merge_unabsorb(nullptr, MLA_BF16, nullptr, nullptr, nullptr, 0, 1, 128, 512, 128, nullptr, nullptr,
+                               nullptr), MLA_OK);
+  EXPECT_EQ(rec.merge_unabsorb, mu_calls);
   EXPECT_EQ(mla_append_cache(Q, Q, (uint16_t*)D, 4096, 64, (int32_t*)D, 64, (int32_t*)D, 64, 1, 512, 64, nullptr),
             MLA_OK);
   EXPECT_EQ(mla_append_cache(Q, Q, (uint16_t*)D, 4096, 64, (int32_t*)D, 64, (int32_t*)D, 64, 0, 512, 64, nullptr),

@@ -246,9 +246,21 @@ def test_merge_validation(lib):
     assert f(None, 0, None, None, 0, 1, 128, 512, None, 0, None, None) == OK
 
 
+def test_merge_unabsorb_validation(lib):
+    f = lib.mla_merge_unabsorb
+    assert f(P16, 0, P16, P16, P16, 2, 1, 128, 256, 128, P16, None, None) == UNSUP   # r
+    assert f(P16, 0, P16, P16, P16, 2, 1, 128, 512, 64, P16, None, None) == UNSUP    # d_V
+    assert f(P16, 2, P16, P16, P16, 2, 1, 128, 512, 128, P16, None, None) == UNSUP   # partial dtype
+    assert f(P16, 0, P16, P16, P16, 2, 1, 129, 512, 128, P16, None, None) == UNSUP   # H
+    assert f(None, 0, P16, P16, P16, 2, 1, 128, 512, 128, P16, None, None) == NULL
+    assert f(P16, 0, P16, P16, P17, 2, 1, 128, 512, 128, P16, None, None) == ALIGN   # w_uv
+    assert f(P16, 0, P16, P16, P16, 2, 1, 128, 512, 128, P17, None, None) == ALIGN   # out
+    assert f(None, 0, None, None, None, 0, 1, 128, 512, 128, None, None, None) == OK  # B = 0: no-op
+
+
 def test_binding_names_match_abi():
     for n in ("mla_absorb_q", "mla_decode_latent", "mla_decode_latent_fp8", "mla_merge_splits",
-              "mla_unabsorb_out", "mla_append_cache",
+              "mla_unabsorb_out", "mla_merge_unabsorb", "mla_append_cache",
               "mla_decode_sparse", "mla_sparse_split_count", "mla_decode_normal", "mla_normal_workspace_size",
               "load_normal_library",
               "mla_decode_workspace_size", "mla_validate_inputs", "mla_status_string"):
@@ -411,6 +423,20 @@ def test_binding_rejects_shape_mismatches():
         mk.mla_decode_latent(q, torch.zeros((2, 1, 4, 64), dtype=bf), kv, bt[:1], sl, 1, 0.07)  # table rows
     with pytest.raises(ValueError):
         mk.mla_unabsorb_out(q, torch.zeros((3, 128, 512), dtype=bf))                           # w_uv heads
+    po = torch.zeros((8, 1, 4, 512), dtype=bf)
+    pl = torch.zeros((8, 1, 4))
+    ind = torch.zeros(3, dtype=torch.int32)
+    w_uv = torch.zeros((4, 128, 512), dtype=bf)
+    with pytest.raises(ValueError):
+        mk.mla_merge_unabsorb(po, pl[:7], ind, w_uv, 2)                                         # lse rows
+    with pytest.raises(ValueError):
+        mk.mla_merge_unabsorb(po, pl, ind[:2], w_uv, 2)                                         # split table
+    with pytest.raises(ValueError):
+        mk.mla_merge_unabsorb(po, pl, ind, w_uv[:3], 2)                                         # w_uv heads
+    with pytest.raises(ValueError):
+        mk.mla_merge_unabsorb(po, pl, ind, w_uv, 2, out=torch.zeros((2, 1, 4, 64)))             # out width
+    with pytest.raises(ValueError):
+        mk.mla_merge_unabsorb(po, pl.double(), ind, w_uv, 2)                                    # lse dtype
     with pytest.raises(ValueError):
         mk.mla_absorb_q(torch.zeros((2, 1, 4, 128), dtype=bf), torch.zeros((4, 128, 512), dtype=bf),
                         q_lat=torch.zeros((2, 1, 4, 256), dtype=bf))
