@@ -3,20 +3,25 @@
 
 One step = the whole path over one batch: absorb (q~ = W_UK^T q_nope) ->
 latent attention over the paged cache (split-KV partials) -> log-sum-exp merge
--> un-absorb (W_UV latent).  Workload: DeepSeek-V3 geometry, B=64 sequences of
+and un-absorb (W_UV latent), in one kernel for bf16 partials and at most four
+splits per sequence, else as two.  Workload: DeepSeek-V3 geometry, B=64 sequences of
 L=4096 cached tokens, T=1, H=128, page size 64 with a seeded random page
 permutation, synthetic N(0,1) bf16 inputs and N(0,1/512) weights.
 
-Timing: W warm-up steps, then K steps between two device synchronisations.
+Timing: untimed warm-up (at least W steps and 0.1 s of back-to-back work, so
+that the clocks, which ramp up over the first ~20 ms after the set-up's idle
+time, have settled), then K steps between two device synchronisations.
 Three replicas of the cache and of the weights rotate from step to step so that
 the 256 MB last-level cache cannot serve a step's reads from the previous one.
 The decode kernel's own duration, from which the roofline fraction is computed,
 is one pair of HIP events on its launch stream around K back-to-back decode
 launches (replicas rotating), divided by K; event pairs around each launch of
 K eager steps are reported beside it (they also span the packet processing
-around the kernel).  The chain throughput (`value`) comes from K replays of the
-step captured as a HIP graph (one graph per replica; `--no-graph` times the
-eager launches instead).  The other workloads, the fp32-partials headline, the
+around the kernel).  The chain throughput (`value`) is the faster of two ways
+of launching the same K steps: eager launches on one stream, and replays of the
+step captured as a HIP graph (one graph per replica; `--no-graph` leaves the
+graph out); `chain_launch` names the one taken and both times are reported.
+The other workloads, the fp32-partials headline, the
 FP8-row, sparse and sparse-FP8 kernels are timed the same way and reported
 under ``detail``; so are a sustained clock/power sample of the headline decode
 kernel and the practical-roof probes (``--roof-seconds``).
@@ -63,6 +68,27 @@ def chain_algorithmic(case, decode_bytes):
     absorb = B * T * H * 128 * 2 + H * 128 * 512 * 2 + B * T * H * 512 * 2
     unabsorb = B * T * H * 512 * 2 + H * 128 * 512 * 2 + B * T * H * 128 * 4
     return decode_bytes + absorb + unabsorb
+
+
+WARM_SECONDS = 0.1
+
+
+def warm_up(fn, n_min, seconds=WARM_SECONDS):
+    """Untimed warm-up: fn(i) for i = 0, 1, ... until at least n_min calls and
+    `seconds` of back-to-back work have passed.  After the host-side set-up the
+    GPU sits idle and its clocks ramp up again over the first ~20 ms of work (the
+    first 50 steps of the headline chain take 1.7x the steady-state time), so a
+    fixed small count would time part of the ramp."""
+    import torch
+    i = 0
+    t0 = time.perf_counter()
+    while i < n_min or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
 
 
 def sparse_algorithmic(sc, row_bytes=ROW_BYTES):
@@ -123,15 +149,16 @@ def bench_sparse(name, K, W, R, dev, fp8=False):
                                 buf.split_indptr, BT, out_latent=lat.view(BT, 1, sc.H, 512),
                                 lse=lse.view(BT, 1, sc.H))
 
-    for i in range(W):
+    warm_up(lambda i: run(i % R), W)
+    t0 = time.perf_counter()      # decode + merge, launched eagerly
+    for i in range(K):
         run(i % R)
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t0 = time.perf_counter()
     for i in range(K):
         run(i % R, evs[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     us_pairs = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     # the kernel's duration: K launches back to back between one event pair
     eb = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -206,9 +233,7 @@ def bench_fp8(name, S, K, W, R, dev):
             ev[1].record(stream)
         mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, case.B)
 
-    for i in range(W):
-        run(i % R)
-    torch.cuda.synchronize()
+    warm_up(lambda i: run(i % R), W)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for i in range(K):
         run(i % R, evs[i])
@@ -703,12 +728,17 @@ def cpu_baseline(case, pairs_n, threads, gpu_out=None, seed=123):
 
 
 def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
+    # merge and un-absorb in one kernel where that is the faster form: bf16
+    # partials and at most four splits per sequence (measured A/B, interleaved,
+    # on the headline: 104.8 against 109.6 us per step; with more splits per
+    # row the fused kernel merges row by row and the two kernels are faster)
     """Time one workload's step (absorb -> decode -> merge -> un-absorb) on the
-    GPU: R replicas of the cache and weights rotate from step to step; K eager
-    steps with HIP events around the decode launch on its stream give the
-    decode kernel's own duration (with automatic splits it includes the
-    one-workgroup plan kernel); K replays of the step captured as a HIP graph
-    (one per replica) give the chain's time per step."""
+    GPU: R replicas of the cache and weights rotate from step to step.  The
+    chain's time per step is the faster of K eager steps and K replays of the
+    step captured as a HIP graph (one per replica); K further eager steps with
+    HIP events around each decode launch, and K back-to-back decode launches
+    between one event pair, give the decode kernel's own duration (with
+    automatic splits it includes the one-workgroup plan kernel)."""
     import numpy as np
     import torch
     import mla_latent_kv_amd as mk
@@ -738,7 +768,9 @@ def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
     out = torch.empty((B, T, H, 128), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(r, ev=None):
+    fused_ok = partials == "bf16" and 1 < S <= 4
+
+    def step(r, ev=None, fused=fused_ok):
         mk.mla_absorb_q(q_nope, wuk[r], q_lat=q_lat)
         if ev is not None:
             ev[0].record(stream)
@@ -750,23 +782,40 @@ def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
                                  num_splits=S, buffers=buf, merge=False)
         if ev is not None:
             ev[1].record(stream)
-        if S != 1:
+        if S == 1:
+            mk.mla_unabsorb_out(latent, wuv[r], out=out)
+        elif fused:
+            # merge and un-absorb in one kernel (the merged latent stays on chip)
+            mk.mla_merge_unabsorb(buf.part_out, buf.part_lse, buf.split_indptr, wuv[r], B, out=out, lse=lse)
+        else:
             mk.mla_merge_splits(buf.part_out, buf.part_lse, buf.split_indptr, B, out_latent=latent,
                                 lse=lse)
-        mk.mla_unabsorb_out(latent, wuv[r], out=out)
+            mk.mla_unabsorb_out(latent, wuv[r], out=out)
 
-    for i in range(W):
+    warm_up(lambda i: step(i % R), W)
+    # the chain launched eagerly: K steps between two synchronisations
+    t0 = time.perf_counter()
+    for i in range(K):
         step(i % R)
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # the same with the other form of the merge and un-absorb (context)
+    alt_ms = None
+    if S != 1:
+        t0s = time.perf_counter()
+        for i in range(K):
+            step(i % R, fused=not fused_ok)
+        torch.cuda.synchronize()
+        alt_ms = (time.perf_counter() - t0s) * 1e3 / K
+    # the same with an event pair around each decode launch (per-launch detail)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t0 = time.perf_counter()
     for i in range(K):
         step(i % R, evs[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     res = {"case": case, "kv": kv, "block_table": block_table, "seqlens": seqlens, "out": out,
            "dec_ms": [a.elapsed_time(b) for a, b in evs], "eager_ms_per_step": (t1 - t0) * 1e3 / K,
-           "warm_ms": None}
+           "warm_ms": None, "graph_ms_per_step": None, "alt_merge_ms_per_step": alt_ms,
+           "merge_unabsorb": "fused" if fused_ok else ("separate" if S != 1 else "none")}
 
     # the decode kernel's own duration: K launches back to back (replicas still
     # rotating) between one event pair, divided by K.  (An event pair around each
@@ -778,8 +827,7 @@ def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
         else:
             mk.mla_decode_latent(q_lat, q_pe, kv[r], block_table, seqlens, max_seqlen, scale,
                                  num_splits=S, buffers=buf, merge=False)
-    for i in range(min(W, 3)):
-        decode_only(i % R)
+    warm_up(lambda i: decode_only(i % R), 3, seconds=0.02)
     eb = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     eb[0].record(stream)
     for i in range(K):
@@ -796,6 +844,7 @@ def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
         torch.cuda.synchronize()
         res["warm_ms"] = float(np.median([a.elapsed_time(b) for a, b in wev]))
     res["ms_per_step"] = res["eager_ms_per_step"]
+    res["chain_launch"] = "eager"
     if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -809,16 +858,17 @@ def time_workload(wl, S, partials, K, W, R, dev, graph=True, warm=False):
             with torch.cuda.graph(g):
                 step(r)
             graphs.append(g)
-        for i in range(W):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
+        warm_up(lambda i: graphs[i % R].replay(), W)
         t0 = time.perf_counter()
         for i in range(K):
             graphs[i % R].replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        res["ms_per_step"] = (t1 - t0) * 1e3 / K
+        res["graph_ms_per_step"] = (t1 - t0) * 1e3 / K
         res["graphs"] = graphs
+        if res["graph_ms_per_step"] < res["ms_per_step"]:
+            res["ms_per_step"] = res["graph_ms_per_step"]
+            res["chain_launch"] = "hip_graph"
     return res
 
 
@@ -841,7 +891,8 @@ def workload_line(wl, S, partials, K, W, R, dev):
         "decode_hbm_frac": nbytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "decode_tflops": flops / (dec_ms * 1e-3) / 1e12,
         "decode_mfma_frac": flops / (dec_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "chain_us_per_step": tw["ms_per_step"] * 1e3,
+        "chain_us_per_step": tw["ms_per_step"] * 1e3, "chain_launch": tw["chain_launch"],
+        "chain_merge_unabsorb": tw["merge_unabsorb"],
         "tokens_per_s": case.B * case.T / (tw["ms_per_step"] * 1e-3),
         "chain_TBps": chain_algorithmic(case, nbytes) / (tw["ms_per_step"] * 1e-3) / 1e12,
     }
@@ -853,8 +904,10 @@ def workload_line(wl, S, partials, K, W, R, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed warm-up steps before each timed region (at least; warm-up also lasts at "
+                         "least 0.1 s of back-to-back work, for the clocks to settle)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--splits", type=int, default=4,
                     help="split-KV chunks per sequence (0 = automatic)")
@@ -952,8 +1005,8 @@ def main():
     kpe_new = torch.randn((B, T, 64), device=dev).to(torch.bfloat16)
     # (a few-microsecond kernel: one event pair around K back-to-back launches)
     app_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    for i in range(args.warmup):
-        mk.mla_append_cache(c_new, kpe_new, kv[i % R], block_table, seqlens)
+    warm_up(lambda i: mk.mla_append_cache(c_new, kpe_new, kv[i % R], block_table, seqlens), args.warmup,
+            seconds=0.02)
     app_ev[0].record(stream)
     for i in range(K):
         mk.mla_append_cache(c_new, kpe_new, kv[i % R], block_table, seqlens)
@@ -1040,8 +1093,11 @@ def main():
             "decode_alg_flops": dec_flops,
             "decode_tflops": dec_flops / (dec_ms_avg * 1e-3) / 1e12,
             "decode_mfma_frac": dec_flops / (dec_ms_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "chain_launch": "eager" if args.no_graph else "hip_graph",
+            "chain_launch": tw["chain_launch"],
             "chain_eager_ms_per_step": eager_ms_per_step,
+            "chain_graph_ms_per_step": tw["graph_ms_per_step"],
+            "chain_merge_unabsorb": tw["merge_unabsorb"],
+            "chain_eager_other_merge_unabsorb_ms_per_step": tw["alt_merge_ms_per_step"],
             "chain_alg_bytes": chain_algorithmic(case, dec_bytes),
             "chain_TBps": chain_algorithmic(case, dec_bytes) / (ms_per_step * 1e-3) / 1e12,
             "append_us": app_ms * 1e3,
