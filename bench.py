@@ -606,13 +606,18 @@ def traffic_record(fetch_csv, write_csv):
     fetch_d = per_dispatch(fetch_csv, "FETCH_SIZE")
     write_d = per_dispatch(write_csv, "WRITE_SIZE")
     # the 1 GiB device-to-device copies (the context measurement and the
-    # calibration copy) are the copy dispatches that wrote exactly 2^20 KiB; the
-    # two passes launch the same dispatches in the same order
-    cal = [key for key, v in write_d.items() if "copyBuffer" in key[0] and v == float(1 << 20)]
-    if not cal or any(key not in fetch_d for key in cal):
+    # calibration copy) are the copy dispatches that wrote exactly 2^20 KiB.  The
+    # two passes make the same copies in the same order (the warm-up loops, whose
+    # length depends on time, launch no copies), so a copy is matched across the
+    # passes by its position among the copy dispatches
+    def copies(d):
+        return [v for (k, _), v in sorted(d.items(), key=lambda kv: kv[0][1]) if "copyBuffer" in k]
+    fc, wc = copies(fetch_d), copies(write_d)
+    cal = [i for i, v in enumerate(wc) if v == float(1 << 20)]
+    if not cal or len(fc) != len(wc):
         raise SystemExit("no 1 GiB calibration copy in both counter passes (run bench.py with --copy-calibration)")
-    fetch_factor = (1 << 30) / (statistics.median(fetch_d[k] for k in cal) * 1024)   # bytes per counted KiB
-    write_factor = (1 << 30) / (statistics.median(write_d[k] for k in cal) * 1024)
+    fetch_factor = (1 << 30) / (statistics.median(fc[i] for i in cal) * 1024)   # bytes per counted KiB
+    write_factor = (1 << 30) / (statistics.median(wc[i] for i in cal) * 1024)
     fetch, write = {}, {}
     for (k, _), v in fetch_d.items():
         fetch.setdefault(k, []).append(v)
@@ -631,6 +636,14 @@ def traffic_record(fetch_csv, write_csv):
         with open(os.path.join(ROOT, "profiles", fname), "w") as fh:
             json.dump(rec, fh, indent=1)
         out.append(rec)
+    # the step's other kernels in the same passes: printed, not recorded
+    for kname in sorted(set(fetch) & set(write)):
+        if kname in TRAFFIC_RECORDS or "copyBuffer" in kname:
+            continue
+        rd = statistics.median(fetch[kname]) * 1024 * fetch_factor
+        wr = statistics.median(write[kname]) * 1024 * write_factor
+        out.append({"kernel": kname, "context": True, "bytes_per_launch": rd + wr, "read_bytes": rd,
+                    "write_bytes": wr, "dispatches": len(fetch[kname])})
     return out
 
 
