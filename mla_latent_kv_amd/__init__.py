@@ -57,6 +57,9 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run mla_latent_kv_amd._build.build()")
+    # torch first: the library then binds to the HIP runtime torch has loaded
+    # (loaded before torch, its HIP calls found no device)
+    _torch()
     L = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     SZ = ctypes.c_size_t
@@ -92,6 +95,7 @@ def load_normal_library():
         return _normal_lib
     if not os.path.exists(NORMAL_LIB_PATH):
         raise ImportError(f"{NORMAL_LIB_PATH} is not built; run mla_latent_kv_amd._build.build()")
+    _torch()   # (as in load_library)
     L = ctypes.CDLL(NORMAL_LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.mla_normal_workspace_size.argtypes = [I, I, I, I, I, P]
