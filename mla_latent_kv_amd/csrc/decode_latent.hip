@@ -1087,11 +1087,39 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     const int rows_here = min(kStageRows, n_rows - round * kStageRows);
     char* const dst = dst_base + (size_t)round * kStageRows * kRowOut;
     constexpr int kChunksPerRow = kRowOut / 16;
-    for (int xx = threadIdx.x; xx < rows_here * kChunksPerRow; xx += 256) {
+    auto out_chunk = [&](int xx, u32x4& v) {   // staged chunk xx -> v (bf16: halves back in order)
       const int r = xx / kChunksPerRow, c = xx - r * kChunksPerRow;
-      u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16));
-      if (!OUT_F32 && ((r >> 4) & 1)) v = u32x4{v[2], v[3], v[0], v[1]};
-      *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = v;
+      v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(tiles_lds + r * kRowOut + ((c ^ (r & 15)) * 16));
+      return r;
+    };
+    if (rows_here == kStageRows) {
+      // a whole block (every unit of a 128-row group): 32 chunks per thread, 16
+      // LDS reads in flight before their stores (one at a time, each read's wait
+      // would stand between consecutive stores)
+      constexpr int kPer = kStageRows * kChunksPerRow / 256, kBatch = 16;
+      static_assert(kPer % kBatch == 0, "whole batches");
+#pragma unroll
+      for (int g = 0; g < kPer / kBatch; ++g) {
+        u32x4 v[kBatch];
+        int rr[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) rr[k] = out_chunk(threadIdx.x + 256 * (kBatch * g + k), v[k]);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const int xx = threadIdx.x + 256 * (kBatch * g + k);
+          const int r = rr[k], c = xx - r * kChunksPerRow;
+          u32x4 o = v[k];
+          if (!OUT_F32 && ((r >> 4) & 1)) o = u32x4{o[2], o[3], o[0], o[1]};
+          *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = o;
+        }
+      }
+    } else {
+      for (int xx = threadIdx.x; xx < rows_here * kChunksPerRow; xx += 256) {
+        u32x4 v;
+        const int r = out_chunk(xx, v), c = xx - r * kChunksPerRow;
+        if (!OUT_F32 && ((r >> 4) & 1)) v = u32x4{v[2], v[3], v[0], v[1]};
+        *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = v;
+      }
     }
     if (round + 1 < 128 / kStageRows) barrier();
   }
