@@ -1,9 +1,9 @@
 """Pins of the CPU oracle to facts fixed outside itself (no GPU).
 
 What pins what:
-* the numpy parity script printed on "MLA in full detail" (expanded and
-  absorbed scores/outputs agree in float64; scale (key+rope)^-0.5; row-vector
-  weight orientation) -- rebuilt here from its printed shapes and seed;
+* the identity "MLA in full detail" states for the absorbed form (expanded and
+  absorbed scores and outputs agree; scale (key + rope)^-0.5), checked on this
+  project's own draws against a direct matrix evaluation;
 * an independent numpy Normal path and PyTorch's float64
   scaled_dot_product_attention on explicitly expanded K/V (library special case);
 * associativity: absorbed mirror == Normal path (M5.8 0x04);
@@ -101,7 +101,8 @@ def test_absorbed_equals_expanded_attention_on_a_tiny_head():
 def test_page_causal_pair_count_from_uniform_weights():
     """With zero queries every visible key gets the same weight, so exp(lse)
     counts the visible keys of each query row.  3 new tokens after a prefix of
-    5 give 3*5 + 3*4/2 = 21 pairs ("MLA in full detail", numpy script)."""
+    5 give 3*5 + 3*4/2 = 21 pairs (the causal visibility of "MLA in full detail",
+    Step 3)."""
     case = tiny(3, B=1, T=3, H=2, lengths=(8,))
     case.q_nope[:] = 0
     case.q_pe[:] = 0
