@@ -589,10 +589,23 @@ def softmax_scale(d_nope=D_NOPE, d_rope=D_ROPE) -> float:
 def absorbed_decode(q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seqlens, max_seqlen,
                     num_splits=1, buffers=None, latent_dtype=None, stream=None):
     """One decode step: absorb -> latent attention (-> merge) -> un-absorb.
+    With 2 to 4 uniform splits and a bf16 latent the partials are bf16 and the
+    merge and un-absorb run as one kernel (mla_merge_unabsorb), the faster form
+    for that case; otherwise as mla_merge_splits (inside the decode call) and
+    mla_unabsorb_out.
 
     Returns (out [B,T,H,128] f32, lse [B,T,H] f32)."""
     torch = _torch()
     q_lat = mla_absorb_q(q_nope, w_uk, stream=stream)
+    if 2 <= num_splits <= 4 and latent_dtype in (None, torch.bfloat16):
+        B, T, H = q_nope.shape[:3]
+        if buffers is None:
+            buffers = DecodeBuffers(B, T, H, max_seqlen, kv_cache.shape[1], num_splits, q_nope.device,
+                                    part_dtype=torch.bfloat16)
+        mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen, softmax_scale(),
+                          num_splits=num_splits, buffers=buffers, merge=False, stream=stream)
+        return mla_merge_unabsorb(buffers.part_out, buffers.part_lse, buffers.split_indptr, w_uv, B,
+                                  stream=stream)
     lat, lse = mla_decode_latent(q_lat, q_pe, kv_cache, block_table, seqlens, max_seqlen,
                                  softmax_scale(), num_splits=num_splits,
                                  out_dtype=latent_dtype or torch.bfloat16, buffers=buffers,

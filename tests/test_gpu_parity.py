@@ -129,8 +129,8 @@ def test_unabsorb(mk, name, latent_f32):
 @pytest.mark.parametrize("S", [1, 4])
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_end_to_end_vs_normal_path(mk, name, S):
-    """S = 1: absorb, decode, un-absorb; S = 4: absorb, split decode, merge,
-    un-absorb."""
+    """S = 1: absorb, decode, un-absorb; S = 4: absorb, split decode with bf16
+    partials, merge and un-absorb in one kernel."""
     import torch
     log(f"[end-to-end] {name} S={S}")
     case = _case(name)
