@@ -116,6 +116,19 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// 16-byte global store with the non-temporal (streaming) hint, for output
+// written once at the end of a launch and read only by a later one.  The
+// compiler has no equivalent form on this target (its nontemporal store keeps
+// the default policy).  The store counts on the vector-memory counter like any
+// other, so the compiler's own waits stay conservative around it.  The data
+// of a store wider than 8 bytes is read from its VGPRs after the instruction
+// issues: a vector instruction that writes them next needs wait states between
+// the two, which the compiler inserts for its own stores but cannot for one in
+// inline assembly -- hence the s_nop inside the statement.
+__device__ __forceinline__ void store16_nt(void* dst, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Workgroup barrier without the memory fence that __syncthreads() adds (the

@@ -1040,7 +1040,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // ---- store: the workgroup's rows [row0, row0 + 128) of its output are one
   // contiguous block (1 KB per row in bf16, 2 KB in fp32).  The normalised
   // accumulators are staged through the (now idle) step ring in row-major
-  // order, then written with 16-byte-per-lane contiguous stores.  Staging
+  // order, then written with 16-byte-per-lane contiguous stores that carry the
+  // streaming hint (every unit writes its block at the same moment, at the end
+  // of the launch; the hint lets the writes drain faster).  Staging
   // swizzle: 16-byte chunk c of staged row r sits at chunk c ^ (r & 15); in the
   // bf16 layout the two 8-byte halves of a chunk are also swapped when bit 4 of
   // r is set (both make the staging writes and the reads conflict-free).
@@ -1110,7 +1112,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
           const int r = rr[k], c = xx - r * kChunksPerRow;
           u32x4 o = v[k];
           if (!OUT_F32 && ((r >> 4) & 1)) o = u32x4{o[2], o[3], o[0], o[1]};
-          *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = o;
+          store16_nt(dst + (size_t)r * kRowOut + 16 * c, o);
         }
       }
     } else {
@@ -1118,7 +1120,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         u32x4 v;
         const int r = out_chunk(xx, v), c = xx - r * kChunksPerRow;
         if (!OUT_F32 && ((r >> 4) & 1)) v = u32x4{v[2], v[3], v[0], v[1]};
-        *(u32x4*)(dst + (size_t)r * kRowOut + 16 * c) = v;
+        store16_nt(dst + (size_t)r * kRowOut + 16 * c, v);
       }
     }
     if (round + 1 < 128 / kStageRows) barrier();
