@@ -569,6 +569,82 @@ def power_roof(seconds, dev):
     return out
 
 
+def pipeline_roof(seconds, dev):
+    """The decode kernel's data flow without its arithmetic, at the headline's
+    shape (pipe_kernel of libmla_probe.so: 256 work units of 1024 tokens = 16
+    randomly placed pages each, 36 KB tiles through a ring of four, a barrier
+    per step), run back to back for `seconds` per variant with the gfx clock
+    and socket power sampled: the stream alone, with the unit's 128 KB output
+    block written at the end (plain and streaming stores), with the 68 MFMAs per
+    wave and step fed from LDS, and with both; then the decode kernel itself
+    (clock_sample).  Three page sets rotate, so the last-level cache cannot
+    serve a launch from the previous one."""
+    import ctypes
+    import numpy as np
+    import torch
+    from mla_latent_kv_amd import _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.mla_pipe_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    units, ppu, sets = 256, 16, 3
+    page_bytes = 64 * 1152
+    npages = sets * units * ppu
+    pool = torch.randn(npages * page_bytes // 2, dtype=torch.float32, device=dev).to(torch.bfloat16)
+    perm = np.random.default_rng(4242).permutation(npages).astype(np.int32).reshape(sets, units, ppu)
+    assert 0 <= perm.min() and perm.max() < npages
+    pages = [torch.from_numpy(perm[k].copy()).to(dev) for k in range(sets)]
+    out = torch.empty(units * 131072, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    tile_bytes = units * 2 * ppu * 32 * 1152
+    rows = []
+    for name, flags in (("stream", 0), ("stream, output block written", 2),
+                        ("stream, output block written with streaming stores", 6), ("stream and MFMAs", 1),
+                        ("stream and MFMAs, output block written", 3),
+                        ("stream and MFMAs, output block written with streaming stores", 7)):
+        def launch(i):
+            st = lib.mla_pipe_probe_launch(ctypes.c_void_p(pool.data_ptr()), npages,
+                                           ctypes.c_void_p(pages[i % sets].data_ptr()), units, ppu, flags,
+                                           ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                           ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"pipeline probe launch failed: hipError {st}")
+        for i in range(6):
+            launch(i)
+        torch.cuda.synchronize()
+        sampler = MetricsSampler().start()
+        time.sleep(0.2)
+        evs, n = [], 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(32):
+                launch(n)
+                n += 1
+            e1.record(stream)
+            evs.append((e0, e1))
+            if len(evs) > 2:
+                evs[-3][1].synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sampler.stop()
+        us = float(np.median([a.elapsed_time(b) for a, b in evs[1:]])) * 1e3 / 32
+        summ = sampler.summary(t0 + 0.3, t1 - 0.05, ["current_gfxclks_mean", "current_socket_power", "current_uclk"])
+        rows.append({"probe": name, "flags": flags, "launch_us": us, "tile_TBps": tile_bytes / (us * 1e-6) / 1e12,
+                     "gfxclk_MHz": summ.get("current_gfxclks_mean", {}).get("median"),
+                     "socket_power_W": summ.get("current_socket_power", {}).get("median"),
+                     "uclk_MHz": summ.get("current_uclk", {}).get("median"),
+                     "sampler_error": sampler.error})
+    del pool, out
+    torch.cuda.empty_cache()
+    dec = clock_sample(seconds, "bf16", dev)
+    dec["probe"] = "decode kernel (headline, 4 splits, bf16 partials)"
+    rows.append(dec)
+    return rows
+
+
 # decode kernel instantiation -> (workload, splits, partials, record file) in a
 # run of `bench.py --no-cpu --no-workloads --roof-seconds 0 --copy-calibration`
 TRAFFIC_RECORDS = {
@@ -958,6 +1034,9 @@ def main():
     ap.add_argument("--trace-segments", metavar="KERNEL_TRACE_CSV",
                     help="instead of the benchmark line: each decode kernel's mean duration over all dispatches and "
                          "over its back-to-back segment, from a rocprofv3 kernel-trace CSV")
+    ap.add_argument("--pipeline-roof", type=float, default=0.0,
+                    help="instead of the benchmark line: run the decode kernel's data flow without its arithmetic "
+                         "(and the decode kernel) back to back for this many seconds each (one JSON line each)")
     ap.add_argument("--power-roof", type=float, default=0.0,
                     help="instead of the benchmark line: run the practical-roof probes for this many seconds each "
                          "(one JSON line per probe)")
@@ -988,6 +1067,10 @@ def main():
         Ts = [int(x) for x in args.crossover_T.split(",")]
         for row in crossover(Ts, args.crossover_S, args.crossover_B, max(3, min(args.steps, 20)),
                              max(1, min(args.warmup, 3)), dev):
+            print(json.dumps(row), flush=True)
+        return
+    if args.pipeline_roof > 0:
+        for row in pipeline_roof(args.pipeline_roof, dev):
             print(json.dumps(row), flush=True)
         return
     if args.power_roof > 0:

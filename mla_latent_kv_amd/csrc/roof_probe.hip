@@ -22,11 +22,30 @@
 // clock and power, gives the MFMA rate and the HBM rate the part sustains at
 // its power limit for a given FLOP/byte mix.
 //
+// A second kernel, pipe_kernel, is the decode kernel's data flow with its
+// arithmetic taken out, to split the decode's time into parts: per work unit
+// (one workgroup of four waves, one per CU), 32-token tiles of 36 KB read from
+// pages of 64 rows of 1152 bytes placed anywhere in the pool (a page list per
+// unit), direct-to-LDS through a ring of four tiles issued three steps ahead,
+// each wave waiting for its own loads of the step and one barrier per step,
+// as the decode kernel does.  Flags add, one at a time:
+//   1  68 bf16 MFMAs 32x32x16 per wave and step, B operands (1 KB per MFMA)
+//      read from the current tile one group of four ahead;
+//   2  at the end, the unit's 128 KB output block written from LDS to `out`
+//      (the decode's split partials), 32 stores of 16 bytes per thread;
+//   4  with 2: those stores with the streaming hint.
+//
 // extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters,
 //                                 int mode, int ratio, float* sink, void* stream)
 //   src: device buffer of at least grid * slice bytes, slice a multiple of 4 KB
 //   and at least 32 KB; mode 0..4; iters even; ratio 1..64; sink: 256 floats (never
 //   written for these inputs; keeps the results live).  Returns a hipError_t.
+// extern "C" int mla_pipe_probe_launch(const void* pool, size_t pool_pages, const int* pages,
+//                                      int units, int pages_per_unit, int flags, void* out,
+//                                      float* sink, void* stream)
+//   pool: pool_pages pages of 73,728 bytes; pages: units x pages_per_unit page
+//   ids, each below pool_pages (not checked on the device); 2 * pages_per_unit
+//   steps per unit; out: units x 128 KB (written only with flag 2); flags 0..7.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,6 +53,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* base, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
@@ -122,7 +142,106 @@ __global__ __launch_bounds__(256, 1) void roof_kernel(const uint8_t* src, size_t
   if (s == 1.2345e30f) sink[threadIdx.x] = s;   // never true for these inputs: keeps the MFMAs live
 }
 
+constexpr int kRowB = 1152, kTileB = 32 * kRowB, kHalfB = kTileB / 2, kPageB = 2 * kTileB;
+constexpr int kRing = 4;   // tiles in the LDS ring (147,456 bytes)
+
+__global__ __launch_bounds__(256, 1) void pipe_kernel(const uint8_t* pool, const int* pages, int ppu, int flags,
+                                                      uint8_t* out, float* sink) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
+  const int hw = w >> 1, pw = w & 1;   // wave w loads 9 of the 18 1 KB chunks of half hw of a tile
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  // page ids through the constant address space: scalar loads, which the
+  // compiler waits for on their own counter (a vector load's wait would also
+  // wait for the tile loads in flight)
+  typedef const __attribute__((address_space(4))) int cint;
+  const cint* pg = (const cint*)(uintptr_t)(pages + (size_t)blockIdx.x * ppu);
+  const int steps = 2 * ppu;
+  auto issue = [&](int it) {
+    const int page = pg[min(it >> 1, ppu - 1)];   // past the last step: the last page again
+    const uint8_t* base = pool + (size_t)page * kPageB;
+    const uint32_t dst = ring + (uint32_t)((it % kRing) * kTileB + hw * kHalfB);
+#pragma unroll
+    for (int n = 0; n < 9; ++n) {
+      const int c = pw + 2 * n;
+      dma16s((uint32_t)((it & 1) * kTileB + hw * kHalfB + c * 1024 + 16 * l), base,
+             __builtin_amdgcn_readfirstlane(dst + c * 1024));
+    }
+  };
+  f32x16 a0 = {}, a1 = {};
+  bf16x8 x;
+  for (int e = 0; e < 8; ++e) x[e] = (__bf16)(0.001f * (l + e));
+  for (int it = 0; it < kRing - 1; ++it) issue(it);
+  for (int it = 0; it < steps; ++it) {
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");   // this wave's 9 loads of step it (18 later ones in flight)
+    __syncthreads();                                      // every wave's share of tile it is in LDS
+    issue(it + kRing - 1);                                // into the buffer of step it - 1, read by all
+    if (flags & 1) {
+      // reads and waits in inline assembly: plain reads are sunk to their MFMAs
+      // by the compiler, one LDS latency each
+      const uint32_t t = ring + (uint32_t)((it % kRing) * kTileB) + 16u * l;
+      bf16x8 y[2][4];
+      auto rd4 = [&](int g, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          asm volatile("ds_read_b128 %0, %1" : "=v"(y[buf][e]) : "v"(t + (uint32_t)(((4 * g + e) * 1024) % kTileB)));
+      };
+      rd4(0, 0);
+#pragma unroll
+      for (int g = 0; g < 17; ++g) {
+        const int cur = g & 1;
+        if (g + 1 < 17) {
+          rd4(g + 1, cur ^ 1);
+          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(y[cur][0]), "+v"(y[cur][1]), "+v"(y[cur][2]), "+v"(y[cur][3]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(y[cur][0]), "+v"(y[cur][1]), "+v"(y[cur][2]), "+v"(y[cur][3]));
+        }
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y[cur][0], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y[cur][1], a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y[cur][2], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y[cur][3], a1, 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (flags & 2) {
+    __syncthreads();
+    uint8_t* dst = out + (size_t)blockIdx.x * 131072;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      u32x4 v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        v[k] = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(ring + (uint32_t)(16 * (threadIdx.x + 256 * (16 * g + k))));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        u32x4* d = (u32x4*)(dst + 16 * (threadIdx.x + 256 * (16 * g + k)));
+        // (the data of a store wider than 8 bytes is read after issue: the
+        // s_nop keeps the next vector instruction from overwriting it first)
+        if (flags & 4) asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(d), "v"(v[k]) : "memory");
+        else *d = v[k];
+      }
+    }
+  }
+  float s = 0.f;
+  for (int e = 0; e < 16; ++e) s += a0[e] + a1[e];
+  if (s == 1.2345e30f) sink[threadIdx.x] = s;   // never true for these inputs: keeps the MFMAs live
+}
+
 }  // namespace
+
+extern "C" int mla_pipe_probe_launch(const void* pool, size_t pool_pages, const int* pages, int units,
+                                     int pages_per_unit, int flags, void* out, float* sink, void* stream) {
+  if (!pool || !pages || !sink || pool_pages < 1 || units < 1 || pages_per_unit < 1 || flags < 0 || flags > 7 ||
+      ((flags & 2) && !out))
+    return (int)hipErrorInvalidValue;
+  const int lds = kRing * kTileB;
+  hipError_t e = hipFuncSetAttribute((const void*)pipe_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return (int)e;
+  hipLaunchKernelGGL(pipe_kernel, dim3(units), dim3(256), lds, (hipStream_t)stream, (const uint8_t*)pool, pages,
+                     pages_per_unit, flags, (uint8_t*)out, sink);
+  return (int)hipGetLastError();
+}
 
 extern "C" int mla_probe_launch(const void* src, size_t slice, int grid, int iters, int mode, int ratio,
                                 float* sink, void* stream) {
