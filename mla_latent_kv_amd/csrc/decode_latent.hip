@@ -1134,9 +1134,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
 //     units(c) = sum_b clamp(ceil(L_b / c), 1, cap)
 // fit in target_units (the CU count).  With B < target_units the answer is at
 // most c = sum/(target - B) (each sequence rounding up by a whole unit, which
-// always fits) and at least min_chunk; two rounds of a search over that range,
-// 256 candidates a round (four threads per candidate, each counting a quarter
-// of the sequences), find it.  If one unit per sequence
+// always fits) and at least min_chunk; a search over that range, 32 candidates
+// a round (32 threads per candidate, each counting every 32nd sequence, so each
+// thread divides only B/32 times a round: the kernel is one CU's work), narrows
+// it 32-fold a round until it is exact.  If one unit per sequence
 // already exceeds the target, every sequence is one unit.  A sequence's S_b
 // chunks are equal up to the page rounding: chunk_b = ceil(ceil(L_b/S_b)/P)*P.
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
@@ -1188,31 +1189,35 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
                                       ((unsigned long long)(p.target_units - B) * P);
     int hi = (int)min((unsigned long long)kmax, max(per_hi, (unsigned long long)kmin));
     int lo = min(kmin, hi);
-    for (int round = 0; round < 2 && lo < hi; ++round) {
-      const int step = (hi - lo + 256) / 256;  // ceil((hi - lo + 1) / 256)
-      // thread (candidate c, group g) counts the units of sequences b = g mod 4
-      const int c = tid & 255, g = tid >> 8;
+    // Each round: candidates k_c = min(hi, lo + c * step), c < 32, step =
+    // ceil((hi - lo + 1) / 32), so the last is within step of hi.  The answer
+    // lies in (best - step, best] for the smallest feasible candidate best (hi
+    // when none is: hi is always feasible), which is the next range.  lo and hi
+    // come from shared values, so every thread runs the same rounds.
+    while (lo < hi) {
+      const int step = (hi - lo + 32) / 32;  // ceil((hi - lo + 1) / 32)
+      // thread (candidate c, group g) counts the units of sequences b = g mod 32
+      const int c = tid & 31, g = tid >> 5;
       const int k = min(hi, lo + c * step);
-      if (tid < 256) cand_units[tid] = 0;
+      if (tid < 32) cand_units[tid] = 0;
       __syncthreads();
       int units = 0;
-      for (int b = g; b < B; b += 4) units += splits(len(b), (unsigned)k * (unsigned)P);
-      atomicAdd(&cand_units[c], units);
+      for (int b = g; b < B; b += 32) units += splits(len(b), (unsigned)k * (unsigned)P);
+      units += __shfl_xor(units, 32);  // lanes l and l + 32 count for the same candidate
+      if (lane < 32) atomicAdd(&cand_units[c], units);
       __syncthreads();
-      // smallest feasible candidate: per wave, then one atomic per wave
-      if (tid < 256) {
-        int kb = cand_units[tid] <= p.target_units ? k : 0x7fffffff;
+      // smallest feasible candidate (wave 0)
+      if (tid < 64) {
+        int kb = (lane < 32 && cand_units[lane] <= p.target_units) ? k : 0x7fffffff;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) kb = min(kb, __shfl_xor(kb, o));
-        if (lane == 0) atomicMin(&red_best, kb);
+        if (lane == 0) red_best = kb;
       }
       __syncthreads();
-      const int best = min(red_best, hi);  // hi is feasible even when no candidate hit it
-      __syncthreads();
-      if (tid == 0) red_best = 0x7fffffff;
+      const int best = min(red_best, hi);
       hi = best;
       lo = max(lo, best - step + 1);
-      __syncthreads();
+      __syncthreads();  // every thread has read red_best and cand_units before the next round
     }
     kbest = hi;
   }
