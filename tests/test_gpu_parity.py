@@ -338,6 +338,7 @@ def test_validate_inputs(mk):
     (None, 64),                                   # the ragged case above (5 sequences)
     (tuple(range(100, 100 + 37 * 211, 211)), 64),  # 37 sequences, growing lengths
     ((1, 16, 4000, 9000, 70000), 16),            # one very long sequence, small pages
+    ((1, 16, 4000, 9000, 200000), 16),           # a search range of 39 pages: two rounds of 32 candidates
 ])
 def test_auto_split_counts(mk, lengths, page):
     """The automatic split counts equal the rule the header states, evaluated
