@@ -123,8 +123,9 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // other, so the compiler's own waits stay conservative around it.  The data
 // of a store wider than 8 bytes is read from its VGPRs after the instruction
 // issues: a vector instruction that writes them next needs wait states between
-// the two, which the compiler inserts for its own stores but cannot for one in
-// inline assembly -- hence the s_nop inside the statement.
+// the two, which the compiler provides for its own stores (by its schedule or an
+// s_nop) but cannot for one inside inline assembly -- hence the s_nop in the
+// statement.
 __device__ __forceinline__ void store16_nt(void* dst, u32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off nt\n\ts_nop 1" ::"v"(dst), "v"(v) : "memory");
 }
