@@ -645,6 +645,68 @@ def pipeline_roof(seconds, dev):
     return rows
 
 
+def timeline(batches, dev):
+    """Where a launch of the headline decode kernel goes, from inside it: the
+    kernel of libmla_timeline.so (the same source built with
+    MLA_DECODE_TIMELINE) stamps the 100 MHz real-time counter at eight points
+    of every wave's work unit.  `batches` snapshots, each of the last of 300
+    launches back to back (three cache replicas rotating, 4 uniform splits,
+    bf16 partials).  The library must be the one loaded (main() loads it in
+    place of libmla_latent.so for --timeline)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import mla_latent_kv_amd as mk
+    import synth
+    lib = mk.load_library()
+    lib.mla_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    case = synth.make_case(synth.WORKLOADS[HEADLINE], poison=False)
+    kv0 = torch.from_numpy(np.ascontiguousarray(case.kv_cache).view(np.int16)).view(torch.bfloat16).to(dev)
+    kv = [kv0] + [kv0.clone() for _ in range(2)]
+    q_lat = torch.from_numpy(synth.normal_bf16(case.q_nope.shape[:3] + (512,), 9300, std=0.5).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+    q_pe = torch.from_numpy(np.ascontiguousarray(case.q_pe).view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seqlens).to(dev)
+    S, per_batch = 4, 300
+    buf = mk.DecodeBuffers(case.B, case.T, case.H, case.max_seqlen, case.page_size, S, dev,
+                           part_dtype=torch.bfloat16)
+    scale = mk.softmax_scale()
+    units = case.B * S   # one workgroup per unit (128 heads = one row group)
+    host = np.zeros(units * 4 * 8, dtype=np.uint64)
+    phases = ["set-up: length and block-table window read, query loads issued",
+              "first tile loads issued, until the first tile has landed",
+              "the 32 steps", "loop end to the final partial state", "normalisation and staging",
+              "issuing the output stores", "the output stores' drain"]
+    diffs, spans, skews, launch_us = [], [], [], []
+    stream = torch.cuda.current_stream()
+    for b in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(per_batch):
+            mk.mla_decode_latent(q_lat, q_pe, kv[i % 3], bt, sl, case.max_seqlen, scale, num_splits=S, buffers=buf,
+                                 merge=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if lib.mla_timeline_read(host.ctypes.data, host.nbytes) != 0:
+            raise RuntimeError("mla_timeline_read failed")
+        if b == 0:
+            continue   # the first batch follows the set-up's idle time (clock ramp)
+        launch_us.append(e0.elapsed_time(e1) * 1e3 / per_batch)
+        ts = host.reshape(units, 4, 8).astype(np.int64)
+        rel = (ts - ts[:, :, 0].min()) / 100.0   # 100 MHz -> us, from the first unit's start
+        diffs.append(np.diff(rel, axis=2).reshape(-1, 7))
+        spans.append(float(rel[:, :, 7].max()))
+        skews.append(float(rel[:, :, 0].max()))
+    d = np.concatenate(diffs)
+    return {"timeline": HEADLINE, "splits": S, "units": units, "snapshots": len(spans),
+            "launch_us_median_of_batches": float(np.median(launch_us)),
+            "phases_us": {n: {"median": float(np.median(d[:, k])), "p10": float(np.percentile(d[:, k], 10)),
+                              "p90": float(np.percentile(d[:, k], 90))} for k, n in enumerate(phases)},
+            "unit_start_skew_us_median": float(np.median(skews)),
+            "first_start_to_last_store_done_us_median": float(np.median(spans))}
+
+
 # decode kernel instantiation -> (workload, splits, partials, record file) in a
 # run of `bench.py --no-cpu --no-workloads --roof-seconds 0 --copy-calibration`
 TRAFFIC_RECORDS = {
@@ -1034,6 +1096,9 @@ def main():
     ap.add_argument("--trace-segments", metavar="KERNEL_TRACE_CSV",
                     help="instead of the benchmark line: each decode kernel's mean duration over all dispatches and "
                          "over its back-to-back segment, from a rocprofv3 kernel-trace CSV")
+    ap.add_argument("--timeline", type=int, default=0, metavar="BATCHES",
+                    help="instead of the benchmark line: the headline decode kernel's phases timed from inside it "
+                         "(libmla_timeline.so), over this many snapshots (one JSON line)")
     ap.add_argument("--pipeline-roof", type=float, default=0.0,
                     help="instead of the benchmark line: run the decode kernel's data flow without its arithmetic "
                          "(and the decode kernel) back to back for this many seconds each (one JSON line each)")
@@ -1061,8 +1126,14 @@ def main():
     import mla_latent_kv_amd as mk
     import synth
 
+    if args.timeline > 0:
+        from mla_latent_kv_amd import _build
+        mk.LIB_PATH = _build.TIMELINE_LIB   # the instrumented build of the same source, in its place
     mk.load_library()
     dev = "cuda:0"
+    if args.timeline > 0:
+        print(json.dumps(timeline(args.timeline, dev)), flush=True)
+        return
     if args.crossover:
         Ts = [int(x) for x in args.crossover_T.split(",")]
         for row in crossover(Ts, args.crossover_S, args.crossover_B, max(3, min(args.steps, 20)),

@@ -5,7 +5,10 @@
 * libmla_normal.so  -- the Normal-path comparison (include/mla_normal.h), whose
   up-projection GEMMs are rocBLAS calls;
 * libmla_probe.so   -- the benchmark's practical-roof probe (csrc/roof_probe.hip),
-  not part of the decode path.
+  not part of the decode path;
+* libmla_timeline.so -- libmla_latent.so with the decode kernel built with
+  MLA_DECODE_TIMELINE: each wave stamps the real-time counter at eight points
+  of its work unit (bench.py --timeline reads them); not for production use.
 """
 from __future__ import annotations
 
@@ -20,14 +23,25 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla_latent.so")
 NORMAL_LIB = os.path.join(HERE, "libmla_normal.so")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
-# library -> (sources, extra link flags)
+TIMELINE_LIB = os.path.join(HERE, "libmla_timeline.so")
+TIMELINE = ("decode_latent.hip", "MLA_DECODE_TIMELINE")   # (source, macro) of the timeline build
+_PATH_SOURCES = ["api.cpp", "decode_latent.hip", "merge_splits.hip", "merge_unabsorb.hip", "bmm.hip",
+                 "append.hip", "noalloc.hip"]
+# library -> (sources, extra link flags); a source given as (file, macro) is
+# compiled with that macro defined, into an object of its own
 LIBRARIES = {
-    LIB: (["api.cpp", "decode_latent.hip", "merge_splits.hip", "merge_unabsorb.hip", "bmm.hip", "append.hip",
-           "noalloc.hip"], []),
+    LIB: (_PATH_SOURCES, []),
     NORMAL_LIB: (["normal_api.cpp", "normal.hip"],
                  ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]),
     PROBE_LIB: (["roof_probe.hip"], []),
+    TIMELINE_LIB: ([TIMELINE if s == TIMELINE[0] else s for s in _PATH_SOURCES], []),
 }
+
+
+def _object(src) -> str:
+    if isinstance(src, tuple):
+        return os.path.join(BUILD, f"{src[0]}.{src[1]}.o")
+    return os.path.join(BUILD, src + ".o")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -53,11 +67,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
     procs = []
-    sources = sorted({src for srcs, _ in LIBRARIES.values() for src in srcs})
+    sources = sorted({src for srcs, _ in LIBRARIES.values() for src in srcs}, key=str)
     for src in sources:
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if src.endswith(".hip"):
+        name, defs = (src[0], [f"-D{src[1]}"]) if isinstance(src, tuple) else (src, [])
+        cmd = [cc, *HIPCC_FLAGS, *defs, "-c", os.path.join(CSRC, name), "-o", _object(src)]
+        if name.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"]
         if verbose:
             print(" ".join(cmd), file=sys.stderr)
@@ -71,7 +85,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
     for lib, (srcs, flags) in LIBRARIES.items():
         tmp = lib + ".tmp"
-        objs = [os.path.join(BUILD, src + ".o") for src in srcs]
+        objs = [_object(src) for src in srcs]
         subprocess.check_call([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *flags])
         os.replace(tmp, lib)
     return LIB

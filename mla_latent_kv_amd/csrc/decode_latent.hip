@@ -239,6 +239,29 @@ __device__ __forceinline__ int unit_keys(const DecodeParams& p, int bb) {
   }
 }
 
+// Timeline build (MLA_DECODE_TIMELINE, a separate library): every wave of the
+// first 2048 workgroups stamps the 100 MHz real-time counter at eight points
+// of its unit into g_timeline[workgroup][wave][point] -- 0 unit start, 1 query
+// and first loads issued, 2 first tile landed, 3 last step done, 4 partial
+// state final, 5 output block staged, 6 output stores issued, 7 stores done;
+// mla_timeline_read copies the array (the last launch's stamps) to the host.
+// In the ordinary build the points compile to nothing.
+#ifdef MLA_DECODE_TIMELINE
+__device__ unsigned long long g_timeline[2048 * 4 * 8];
+#define MLA_TS(k)                                                                                  \
+  do {                                                                                             \
+    if (blockIdx.x < 2048) g_timeline[((size_t)blockIdx.x * 4 + w) * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define MLA_TS_DRAIN() asm volatile("s_waitcnt vmcnt(0)" ::: "memory")
+#else
+#define MLA_TS(k) \
+  do {            \
+  } while (0)
+#define MLA_TS_DRAIN() \
+  do {                 \
+  } while (0)
+#endif
+
 template <int NB, bool SPLIT, bool OUT_F32, bool SPARSE, bool FP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   static_assert(!FP8 || NB == 3, "FP8 ring: the tiles of steps i, i+1 and the one being converted");
@@ -267,6 +290,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   if (kx >= per_xcd) return;
   const int u = (blockIdx.x & 7) * per_xcd + kx;
   if (u >= n_units) return;
+  MLA_TS(0);
   const int item = u / p.n_rg;
   const int rg = u - item * p.n_rg;
 
@@ -795,6 +819,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   l_part = 0.f;
 #pragma unroll
   for (int cb = 0; cb < kR / 32; ++cb) acc[cb] = f32x16{};
+  MLA_TS(1);
   if (nsteps > 0) for (int pass = 0;; ++pass) {
     if (pass > 0) {
       if constexpr (SPARSE && FP8) {
@@ -867,6 +892,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
         wait_vm<9 * (NB - 2)>();
       }
       barrier();
+      MLA_TS(2);
       if (nsteps == 1 && j1 - j0 < kStepTok) {
         clear_tail(0);
         wait_lgkm0();
@@ -1000,6 +1026,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
       }
       step(i);
     }
+    MLA_TS(3);
     wait_vm0();  // the loads issued past the last step
     mfma_drain();
     wait_lgkm0();
@@ -1016,6 +1043,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     grew = false;
   }
 
+  MLA_TS(4);
   // ---- finalize: row sums (lanes l and l ^ 32 hold halves of each row), lse ----
   float ls;
   {
@@ -1050,6 +1078,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
   // 128w + 32cb + 8q4 + 4hl + e of row 32 rb + (l & 31), rb = (w + ri) & 3.
   wait_lgkm0();
   barrier();
+  MLA_TS(5);
   float inv[4];
 #pragma unroll
   for (int ri = 0; ri < 4; ++ri)
@@ -1125,7 +1154,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(DecodeParams p) {
     }
     if (round + 1 < 128 / kStageRows) barrier();
   }
+  MLA_TS(6);
+  MLA_TS_DRAIN();
+  MLA_TS(7);
 }
+
+#ifdef MLA_DECODE_TIMELINE
+extern "C" int mla_timeline_read(void* host, size_t bytes) {
+  if (!host || bytes > sizeof(g_timeline)) return (int)hipErrorInvalidValue;
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 // ---- automatic split plan: work list (b, j0, j1, slot) and split_indptr ----
 // One workgroup.  The decode launch runs one work unit per CU at a time, so its

@@ -8,7 +8,8 @@ write those registers (the store would write the new value).  The compiler
 keeps that slot clear for its own stores; a store written in inline assembly
 (the decode epilogue's streaming store, the probe's) carries its own wait
 states.  These tests hold both to it, on the code the tests and the benchmark
-actually load."""
+actually load, and check that the decode library proper carries none of the
+timeline build's instrumentation."""
 import os
 import re
 import shutil
@@ -178,3 +179,30 @@ def test_hazard_check_detects_a_planted_case():
     assert not _wide_store_hazards(fixed)
     addr_only = {"k": ["global_store_dwordx4 v[0:1], v[4:7], off", "v_lshl_add_u64 v[0:1], s[0:1], 0, v[8:9]"]}
     assert not _wide_store_hazards(addr_only)
+
+
+@pytest.fixture(scope="module")
+def timeline_code():
+    if not os.path.exists(_build.TIMELINE_LIB):
+        _build.build()
+    return _functions(_disassemble(_build.TIMELINE_LIB))
+
+
+def test_timeline_points_only_in_the_timeline_build(decode_code, timeline_code):
+    """The decode library proper carries no timeline point (the instrumented
+    build of the same source is a library of its own); the timeline build's
+    headline kernel reads the real-time counter at its eight points."""
+    for name, code in decode_code.items():
+        assert not any(i.startswith("s_memrealtime") for i in code), name
+    head = [n for n in timeline_code if n.startswith("_ZN3mla13decode_kernelILi4ELb1ELb0ELb0ELb0E")]
+    assert len(head) == 1
+    assert sum(i.startswith("s_memrealtime") for i in timeline_code[head[0]]) == 8
+
+
+def test_timeline_entry_point_only_in_the_timeline_build():
+    import ctypes
+    if not os.path.exists(_build.TIMELINE_LIB):
+        _build.build()
+    mk.load_library()   # (the HIP runtime first, as for the product library)
+    assert not hasattr(ctypes.CDLL(mk.LIB_PATH), "mla_timeline_read")
+    assert hasattr(ctypes.CDLL(_build.TIMELINE_LIB), "mla_timeline_read")
